@@ -1,0 +1,163 @@
+/*
+ * rs.h — C ABI of the Representation Shift hot path on MI355X (gfx950).
+ *
+ * The method: "Representation Shift: Unifying Token Compression with FlashAttention"
+ * (arXiv HTML page).  A pre-LN Vision/Video Transformer block (Sec. 3.3, Eqs. (5) and
+ * (6)) runs fused attention that never stores the attention map (Sec. 3.1, Eq. (1);
+ * Sec. 1 on fused attention), then its MLP sublayer; every token is scored by the
+ * MLP-sublayer representation shift || MLP(LN(x')) - x' ||_2 (Sec. 3.2, Eq. (4), with
+ * Sec. 3.3 case ii and the L2 distance); the lowest-scoring tokens are dropped, the
+ * same number in every sample (Sec. 3.2, toy experiments; Sec. 4.1 and 4.2 settings).
+ *
+ * Conventions shared by every entry point
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library never
+ *    allocates or frees device memory; scratch space is the caller's `workspace`.
+ *  - Every tensor is dense row-major.  Activations are [B][L][C] (sample, token,
+ *    channel).  A Linear layer's weight is [out][in] and computes z W^T + b.
+ *  - Element type: RS_F32 (float) or RS_BF16 (bfloat16 storage; all accumulation,
+ *    softmax, LayerNorm statistics and scores are fp32).  Scores are always fp32,
+ *    indices int32.
+ *  - Every data pointer must be 16-byte aligned; `workspace` 256-byte aligned.
+ *  - All work is enqueued on `stream` (0 = the null stream) and is asynchronous; the
+ *    call returns once it is enqueued.  Synchronise the stream before reading outputs.
+ *  - Validation is synchronous and happens before anything is enqueued: on an error
+ *    nothing is enqueued, no output is touched and the code is returned.  A failed
+ *    kernel launch returns RS_ERR_HIP (earlier launches of the call may have run).
+ *    Nothing is printed, nothing aborts, no C++ exception crosses the ABI.
+ *    rs_last_error() returns a message for the calling thread's last failure.
+ *  - Calls are re-entrant; concurrent calls need distinct workspaces and outputs.
+ *  - Limits (else RS_ERR_UNSUPPORTED): head dim 64 (C == heads*64), C % 64 == 0,
+ *    hidden % 64 == 0, 1 <= L <= RS_MAX_TOKENS, and B*L*max(3C, hidden) < 2^31.
+ */
+#ifndef RS_H_
+#define RS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RS_MAX_TOKENS 16384
+
+typedef enum {
+  RS_OK = 0,
+  RS_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad schedule */
+  RS_ERR_UNSUPPORTED = 2,   /* shape outside the limits listed above */
+  RS_ERR_WORKSPACE = 3,     /* workspace smaller than rs_workspace_bytes() */
+  RS_ERR_HIP = 4            /* a HIP call or kernel launch failed */
+} rs_status;
+
+typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
+
+/* Shape of one encoder: width C, heads (head dim C/heads = 64), MLP hidden width,
+ * LayerNorm epsilon (biased variance), element type, and whether token 0 is a class
+ * token that selection always keeps. */
+typedef struct {
+  int C;
+  int heads;
+  int hidden;
+  float ln_eps;
+  rs_dtype dtype;
+  int has_cls;
+} rs_model_desc;
+
+/* Weights of one pre-LN block (Sec. 3.3, Eqs. (5) and (6)), all of desc.dtype.
+ * w_qkv rows 0..C-1 produce Q, rows C..2C-1 K, rows 2C..3C-1 V; head h uses rows
+ * h*64 .. h*64+63 of each (Eq. (1) applied per head with scale 1/sqrt(64)).
+ * MLP = fc2(GELU(fc1(.))) with the exact (erf) GELU. */
+typedef struct {
+  const void *ln1_g, *ln1_b;    /* [C]                  */
+  const void *w_qkv, *b_qkv;    /* [3C][C], [3C]        */
+  const void *w_proj, *b_proj;  /* [C][C], [C]          */
+  const void *ln2_g, *ln2_b;    /* [C]                  */
+  const void *w_fc1, *b_fc1;    /* [hidden][C], [hidden] */
+  const void *w_fc2, *b_fc2;    /* [C][hidden], [C]     */
+} rs_block_weights;
+
+/* One block plus selection (Eqs. (5), (6), the MLP-sublayer shift of Eq. (4) and the
+ * per-sample drop of the lowest scores).
+ *  x        [B][L][C]   block input.
+ *  keep_k   tokens kept per sample, 1 <= keep_k <= L (keep_k == L keeps all; the
+ *           class token, when desc->has_cls, counts towards keep_k and is kept).
+ *  y        [B][L][C]   block output x_hat (Eq. (6)); nullable (then not written).
+ *  scores   [B][L]      fp32 || MLP(LN(x')) - x' ||_2 per token; nullable.
+ *  kept_idx [B][keep_k] kept token indices of each sample, ascending.  Order used to
+ *           choose: score descending, ties to the lower index, NaN lowest.
+ *  y_kept   [B][keep_k][C] rows of x_hat at kept_idx (class token first when present).
+ *  workspace/ws_bytes   >= rs_workspace_bytes(desc, 1, B, L). */
+rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
+                           const void* x, int B, int L, int keep_k,
+                           void* y, float* scores, int32_t* kept_idx, void* y_kept,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Representation shift with the L2 distance (Eq. (4)) of given tensors:
+ * scores[r] = || fx[r,:] - x[r,:] ||_2 for every row r of [B*L][C]. */
+rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
+                   float* scores, hipStream_t stream);
+
+/* Per-sample selection and compaction: keep the keep_k highest scores of each sample
+ * (ties to the lower index, NaN lowest, token 0 always kept if has_cls), write their
+ * indices ascending to kept_idx [B][keep_k] and, if x_kept is not null, the rows
+ * x[b, kept_idx[b, j], :] to x_kept [B][keep_k][C].  x may be null when x_kept is. */
+rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C,
+                         rs_dtype dtype, int keep_k, int has_cls,
+                         int32_t* kept_idx, void* x_kept, hipStream_t stream);
+
+/* Whole encoder with progressive pruning (Sec. 4.1 and 4.2 settings): blocks 0..depth-1
+ * in order; after each block listed in prune_layers (0-based, strictly ascending) the
+ * block's output is compacted to the floor(r*L + 1/2) highest-scoring tokens of the
+ * current L (r = the matching keep_ratios entry, 0 < r <= 1, evaluated in IEEE
+ * double), the score being that block's MLP-sublayer shift.
+ *  blocks   [depth] weight sets.
+ *  out      [B][L_final][C] encoder output (L_final from rs_encoder_out_len).
+ *  out_idx  [B][L_final] original token index of every output row.
+ *  workspace/ws_bytes   >= rs_workspace_bytes(desc, depth, B, L). */
+rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* blocks,
+                             int depth, const void* x, int B, int L,
+                             const int* prune_layers, const double* keep_ratios, int n_prune,
+                             void* out, int32_t* out_idx,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Host only: token count after the schedule (same rule as rs_encoder_forward). */
+rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers,
+                             const double* keep_ratios, int n_prune, int* L_final);
+
+/* Host only: workspace bytes that suffice for rs_block_forward and for
+ * rs_encoder_forward (any depth >= 1) at batch B and input length L.  Returns 0 for an
+ * invalid description. */
+size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L);
+
+/* Message for the calling thread's last failed call ("" if none); valid until the next
+ * call on that thread. */
+const char* rs_last_error(void);
+
+/* ---- kernel timing (measurement support; not part of the method) -------------------
+ * Between rs_timing_begin(kernel) and rs_timing_end(), every launch of that kernel
+ * class made by this library is bracketed by HIP events recorded on the stream it is
+ * launched on.  rs_timing_end() waits for those events and returns the summed kernel
+ * time, the number of launches and the summed algorithmic work of those launches
+ * (flop for the GEMM and attention kernels, bytes for the memory-bound ones).
+ * One timing session at a time per process. */
+typedef enum {
+  RS_KERNEL_LAYERNORM = 0,
+  RS_KERNEL_QKV = 1,
+  RS_KERNEL_ATTENTION = 2,
+  RS_KERNEL_PROJ = 3,
+  RS_KERNEL_FC1 = 4,
+  RS_KERNEL_FC2_SCORE = 5,
+  RS_KERNEL_TOPK = 6,
+  RS_KERNEL_GATHER = 7,
+  RS_KERNEL_SCORE = 8,
+  RS_KERNEL_COUNT = 9
+} rs_kernel_id;
+
+rs_status rs_timing_begin(int kernel_id);
+rs_status rs_timing_end(float* total_ms, int* launches, double* work);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RS_H_ */

@@ -1,0 +1,170 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol include/rs.h
+declares, and rejects bad arguments synchronously, before any HIP call (so these
+run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+
+import pytest
+
+from oracle import rs_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def N():
+    from vit_token_pruning_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        from vit_token_pruning_amd import build
+        build.build()
+    _native.lib()
+    return _native
+
+
+def test_every_declared_symbol_is_exported(N):
+    names = N.declared_symbols()
+    assert {"rs_block_forward", "rs_score", "rs_topk_gather", "rs_encoder_forward"} <= set(names)
+    for n in names:
+        assert hasattr(N.lib(), n), n
+
+
+def _desc(N, C=384, heads=6, hidden=1536, dtype=1, has_cls=1, eps=1e-6):
+    return N.ModelDesc(C, heads, hidden, eps, dtype, has_cls)
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+def _weights(N, p=FAKE):
+    return N.BlockWeights(*([p] * 12))
+
+
+def _block_call(N, desc=None, w=None, x=FAKE, B=2, L=197, k=138, y=FAKE, s=FAKE, kept=FAKE,
+                yk=FAKE, ws=FAKE, ws_bytes=None):
+    lib = N.lib()
+    desc = desc if desc is not None else _desc(N)
+    w = w if w is not None else _weights(N)
+    if ws_bytes is None:
+        ws_bytes = lib.rs_workspace_bytes(ctypes.byref(desc), 1, B, L) if desc.C > 0 else 0
+    return lib.rs_block_forward(ctypes.byref(desc), ctypes.byref(w), x, B, L, k, y, s, kept, yk,
+                                ws, ws_bytes, None)
+
+
+def test_block_forward_validation(N):
+    lib = N.lib()
+    E_ARG, E_UNS, E_WS = N.RS_ERR_INVALID_ARG, N.RS_ERR_UNSUPPORTED, N.RS_ERR_WORKSPACE
+    cases = [
+        (dict(desc=_desc(N, dtype=7)), E_ARG),
+        (dict(desc=_desc(N, C=384, heads=4)), E_UNS),          # head dim != 64
+        (dict(desc=_desc(N, C=200, heads=3)), E_UNS),          # C % 64
+        (dict(desc=_desc(N, hidden=1000)), E_UNS),
+        (dict(desc=_desc(N, eps=0.0)), E_ARG),
+        (dict(desc=_desc(N, has_cls=2)), E_ARG),
+        (dict(k=0), E_ARG),
+        (dict(k=198), E_ARG),
+        (dict(L=0, k=1), E_ARG),
+        (dict(L=20000, k=5), E_UNS),
+        (dict(x=None), E_ARG),
+        (dict(x=FAKE + 4), E_ARG),                              # misaligned
+        (dict(kept=None), E_ARG),
+        (dict(yk=None), E_ARG),
+        (dict(w=_weights(N, 0)), E_ARG),
+        (dict(ws=FAKE + 16), E_ARG),                            # workspace not 256-aligned
+        (dict(ws_bytes=1024), E_WS),
+    ]
+    for kw, want in cases:
+        got = _block_call(N, **kw)
+        assert got == want, (kw, got, lib.rs_last_error())
+        assert lib.rs_last_error().decode()
+
+
+def test_score_and_topk_validation(N):
+    lib = N.lib()
+    assert lib.rs_score(FAKE, FAKE, 2, 10, 100, 1, FAKE, None) == N.RS_ERR_UNSUPPORTED  # C % 8
+    assert lib.rs_score(None, FAKE, 2, 10, 64, 1, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_score(FAKE, FAKE, 2, 10, 64, 5, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 0, 1, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 11, 1, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 5, 3, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_topk_gather(None, FAKE, 2, 10, 64, 1, 5, 1, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 3, 1, 5, 1, FAKE, FAKE, None) == N.RS_ERR_UNSUPPORTED
+    assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 5, 1, FAKE, FAKE + 8, None) == N.RS_ERR_INVALID_ARG
+
+
+def test_encoder_schedule_matches_oracle(N):
+    import synth
+    lib = N.lib()
+    for wl in synth.WORKLOADS.values():
+        out = ctypes.c_int()
+        st = lib.rs_encoder_out_len(wl.depth, wl.L, N.int_array(wl.prune_layers),
+                                    N.dbl_array(wl.keep_ratios), len(wl.prune_layers), ctypes.byref(out))
+        assert st == N.RS_OK
+        assert out.value == O.schedule(wl.depth, wl.L, wl.prune_layers, wl.keep_ratios)[2]
+    # round-half-up cases evaluated in double on both sides
+    for r, L in [(0.5, 3), (0.9, 1905), (0.7, 197), (0.65, 83), (0.1, 5), (1.0, 1)]:
+        out = ctypes.c_int()
+        assert lib.rs_encoder_out_len(1, L, N.int_array([0]), N.dbl_array([r]), 1,
+                                      ctypes.byref(out)) == N.RS_OK
+        assert out.value == O.keep_count(r, L)
+
+
+def test_encoder_validation(N):
+    lib = N.lib()
+    out = ctypes.c_int()
+
+    def ol(depth, L, pl, kr):
+        return lib.rs_encoder_out_len(depth, L, N.int_array(pl), N.dbl_array(kr), len(pl), ctypes.byref(out))
+
+    assert ol(12, 197, [3, 3], [0.7, 0.7]) == N.RS_ERR_INVALID_ARG      # not strictly ascending
+    assert ol(12, 197, [6, 3], [0.7, 0.7]) == N.RS_ERR_INVALID_ARG
+    assert ol(12, 197, [12], [0.7]) == N.RS_ERR_INVALID_ARG             # >= depth
+    assert ol(12, 197, [-1], [0.7]) == N.RS_ERR_INVALID_ARG
+    assert ol(12, 197, [1], [0.0]) == N.RS_ERR_INVALID_ARG
+    assert ol(12, 197, [1], [1.5]) == N.RS_ERR_INVALID_ARG
+    assert ol(12, 197, [1], [float("nan")]) == N.RS_ERR_INVALID_ARG
+    assert ol(12, 4, [1], [0.1]) == N.RS_ERR_INVALID_ARG                # keeps 0 tokens
+    assert ol(0, 197, [], []) == N.RS_ERR_INVALID_ARG
+    d = _desc(N)
+    blocks = (N.BlockWeights * 12)(*[_weights(N) for _ in range(12)])
+    ws = lib.rs_workspace_bytes(ctypes.byref(d), 12, 4, 197)
+    assert ws > 0
+    st = lib.rs_encoder_forward(ctypes.byref(d), blocks, 12, FAKE, 4, 197, N.int_array([3, 6, 9]),
+                                N.dbl_array([0.7] * 3), 3, FAKE, FAKE, FAKE, ws - 256, None)
+    assert st == N.RS_ERR_WORKSPACE
+    blocks[5] = _weights(N, 0)
+    st = lib.rs_encoder_forward(ctypes.byref(d), blocks, 12, FAKE, 4, 197, N.int_array([3, 6, 9]),
+                                N.dbl_array([0.7] * 3), 3, FAKE, FAKE, FAKE, ws, None)
+    assert st == N.RS_ERR_INVALID_ARG and b"block 5" in lib.rs_last_error()
+
+
+def test_workspace_query(N):
+    lib = N.lib()
+    assert lib.rs_workspace_bytes(None, 1, 2, 197) == 0
+    bad = _desc(N, C=100)
+    assert lib.rs_workspace_bytes(ctypes.byref(bad), 1, 2, 197) == 0
+    d = _desc(N)
+    a = lib.rs_workspace_bytes(ctypes.byref(d), 1, 256, 197)
+    b = lib.rs_workspace_bytes(ctypes.byref(d), 12, 256, 197)
+    assert a == b and a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
+
+
+def test_timing_session_without_launches(N):
+    lib = N.lib()
+    assert lib.rs_timing_begin(99) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_timing_end(None, None, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_timing_begin(4) == N.RS_OK
+    assert lib.rs_timing_begin(4) == N.RS_ERR_INVALID_ARG
+    ms, n, work = ctypes.c_float(1), ctypes.c_int(1), ctypes.c_double(1)
+    assert lib.rs_timing_end(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)) == N.RS_OK
+    assert ms.value == 0 and n.value == 0 and work.value == 0
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and the HIP sources never name the oracle or the input generators."""
+    pkg = os.path.join(ROOT, "vit_token_pruning_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+                assert "import synth" not in text and "from synth" not in text, f

@@ -1,0 +1,95 @@
+"""GPU parity of the selection kernels through the C ABI: rs_topk_gather (bit-exact
+indices and rows against the oracle's selection) and rs_score (Eq. (4), L2)."""
+import numpy as np
+import pytest
+
+from oracle import rs_oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+# (B, L, k, has_cls, score kind): every stage shape of the four encoder workloads, plus
+# degenerate and maximum sizes
+STAGES = [
+    (256, 197, 138, True), (256, 138, 97, True), (256, 97, 68, True),
+    (128, 197, 128, True), (128, 128, 83, True), (128, 83, 54, True),
+    (8, 1568, 784, False), (8, 784, 392, False), (8, 392, 196, False),
+    (4, 1568, 784, False), (4, 784, 392, False), (4, 392, 196, False), (4, 196, 98, False),
+    (2, 197, 138, True),
+]
+EDGES = [
+    (1, 1, 1, True), (1, 1, 1, False), (3, 5, 5, False), (3, 5, 5, True), (2, 7, 1, True),
+    (2, 7, 1, False), (5, 1000, 1, False), (2, 16384, 1, False), (2, 16384, 16384, True),
+    (2, 16384, 8191, False), (3, 1025, 513, True), (1, 2352, 1882, False),
+]
+
+
+def _run(B, L, k, cls, kind, seed, C=64, inject=True):
+    import torch
+    import vit_token_pruning_amd as rs
+    s = synth.make_scores(B, L, seed, kind)
+    if inject and L >= 6:
+        s[0, 3] = np.nan
+        s[-1, 1] = np.inf
+        s[-1, 2] = -0.0
+        s[-1, 4] = 0.0
+    x = synth.round_to_bf16(np.random.default_rng(seed).standard_normal((B, L, C)).astype(np.float32))
+    sd = torch.from_numpy(s).cuda()
+    xd = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    kept, xk = rs.topk_gather(sd, xd, k, cls)
+    torch.cuda.synchronize()
+    kept = kept.cpu().numpy()
+    xk = xk.float().cpu().numpy()
+    for b in range(B):
+        want = O.select_kept(s[b], k, cls)
+        assert kept[b].tolist() == want, f"sample {b}"
+        np.testing.assert_array_equal(xk[b], x[b][want])
+
+
+@pytest.mark.parametrize("B,L,k,cls", STAGES)
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_topk_gather_stage_shapes(B, L, k, cls, kind):
+    _run(B, L, k, cls, kind, seed=L * 7 + k)
+
+
+@pytest.mark.parametrize("B,L,k,cls", EDGES)
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed"])
+def test_topk_gather_edges(B, L, k, cls, kind):
+    _run(B, L, k, cls, kind, seed=L + 3 * k + B)
+
+
+def test_topk_select_only_and_fp32_rows():
+    import torch
+    import vit_token_pruning_amd as rs
+    s = synth.make_scores(3, 300, 5, "ties")
+    sd = torch.from_numpy(s).cuda()
+    kept, xk = rs.topk_gather(sd, None, 100, False)
+    assert xk is None
+    for b in range(3):
+        assert kept[b].cpu().tolist() == O.select_kept(s[b], 100, False)
+    x = np.random.default_rng(1).standard_normal((3, 300, 192)).astype(np.float32)
+    kept, xk = rs.topk_gather(sd, torch.from_numpy(x).cuda(), 100, True)
+    for b in range(3):
+        want = O.select_kept(s[b], 100, True)
+        np.testing.assert_array_equal(xk[b].cpu().numpy(), x[b][want])
+
+
+@pytest.mark.parametrize("dt,B,L,C", [("bf16", 256, 197, 384), ("bf16", 8, 1568, 768),
+                                      ("f32", 2, 197, 192), ("bf16", 1, 1, 8), ("f32", 3, 77, 1024)])
+def test_score_matches_oracle(dt, B, L, C):
+    import torch
+    import vit_token_pruning_amd as rs
+    rng = np.random.default_rng(B + L + C)
+    a = rng.standard_normal((B, L, C)).astype(np.float32)
+    b = (a + 0.3 * rng.standard_normal((B, L, C))).astype(np.float32)
+    if dt == "bf16":
+        a, b = synth.round_to_bf16(a), synth.round_to_bf16(b)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    s = rs.score(torch.from_numpy(a).cuda().to(tdt), torch.from_numpy(b).cuda().to(tdt))
+    got = s.cpu().numpy().astype(np.float64)
+    want = O.representation_shift(a, b)
+    rel = np.abs(got - want) / want
+    # bar: 1e-2 relative; the arithmetic (exact inputs, fp32 sum of <= 1024 squares) is
+    # good to ~C * 2^-24, so anything above 1e-4 would indicate a defect
+    assert rel.max() <= 1e-4
+    assert rs.score(torch.zeros(2, 3, 64, device="cuda"), torch.zeros(2, 3, 64, device="cuda")).abs().max() == 0

@@ -1,0 +1,199 @@
+"""Representation Shift token pruning on MI355X: torch-facing wrappers of librs.so.
+
+Every function takes CUDA (HIP) torch tensors, checks shapes/dtypes/devices, and
+passes raw pointers plus the current stream to the C ABI of include/rs.h.  Outputs are
+allocated with torch.  No step of the method runs in Python or on the CPU here.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _native as N
+from ._native import BLOCK_FIELDS, KERNELS, RSError, lib  # noqa: F401
+
+__all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forward",
+           "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib"]
+
+_DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
+
+
+class ModelSpec:
+    """Width, heads (head dim 64), MLP hidden width, LN eps, dtype, class token flag."""
+
+    def __init__(self, C: int, heads: int, hidden: int, dtype: torch.dtype = torch.bfloat16,
+                 has_cls: bool = True, ln_eps: float = 1e-6):
+        if dtype not in _DT:
+            raise TypeError(f"dtype must be float32 or bfloat16, got {dtype}")
+        self.C, self.heads, self.hidden, self.dtype = C, heads, hidden, dtype
+        self.has_cls, self.ln_eps = bool(has_cls), float(ln_eps)
+
+    def desc(self) -> N.ModelDesc:
+        return N.ModelDesc(self.C, self.heads, self.hidden, self.ln_eps, _DT[self.dtype],
+                           int(self.has_cls))
+
+    def weight_shapes(self):
+        C, Hd = self.C, self.hidden
+        return {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,),
+                "w_proj": (C, C), "b_proj": (C,), "ln2_g": (C,), "ln2_b": (C,),
+                "w_fc1": (Hd, C), "b_fc1": (Hd,), "w_fc2": (C, Hd), "b_fc2": (C,)}
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _weights(spec: ModelSpec, w: Dict[str, torch.Tensor]) -> N.BlockWeights:
+    shapes = spec.weight_shapes()
+    return N.BlockWeights(*[_dev(w[n], n, spec.dtype, shapes[n]) for n in BLOCK_FIELDS])
+
+
+def workspace_bytes(spec: ModelSpec, depth: int, B: int, L: int) -> int:
+    d = spec.desc()
+    n = lib().rs_workspace_bytes(ctypes.byref(d), depth, B, L)
+    if n == 0:
+        raise ValueError("invalid model description for the workspace query")
+    return int(n)
+
+
+def _workspace(spec, depth, B, L, device):
+    return torch.empty(workspace_bytes(spec, depth, B, L), dtype=torch.uint8, device=device)
+
+
+def block_forward(spec: ModelSpec, w: Dict[str, torch.Tensor], x: torch.Tensor, keep_k: int,
+                  want_y: bool = True, want_scores: bool = True,
+                  workspace: Optional[torch.Tensor] = None):
+    """One pre-LN block plus selection.  x [B, L, C].  Returns a dict with y (block
+    output, or None), scores [B, L] fp32 (or None), kept_idx [B, keep_k] int32 and
+    y_kept [B, keep_k, C]."""
+    B, L, C = x.shape
+    _dev(x, "x", spec.dtype, (B, L, spec.C))
+    dev = x.device
+    y = torch.empty_like(x) if want_y else None
+    s = torch.empty(B, L, dtype=torch.float32, device=dev) if want_scores else None
+    kept = torch.empty(B, keep_k, dtype=torch.int32, device=dev)
+    yk = torch.empty(B, keep_k, C, dtype=x.dtype, device=dev)
+    ws = _workspace(spec, 1, B, L, dev) if workspace is None else workspace
+    d, wt = spec.desc(), _weights(spec, w)
+    N.check("rs_block_forward", lib().rs_block_forward(
+        ctypes.byref(d), ctypes.byref(wt), x.data_ptr(), B, L, keep_k,
+        y.data_ptr() if y is not None else None, s.data_ptr() if s is not None else None,
+        kept.data_ptr(), yk.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return {"y": y, "scores": s, "kept_idx": kept, "y_kept": yk}
+
+
+def score(fx: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
+    """|| fx - x ||_2 per row over the last axis; fx, x [B, L, C] -> [B, L] fp32."""
+    if fx.shape != x.shape or fx.dtype != x.dtype or x.dim() != 3:
+        raise ValueError("fx and x must be [B, L, C] tensors of one shape and dtype")
+    B, L, C = x.shape
+    _dev(fx, "fx", x.dtype)
+    _dev(x, "x", x.dtype)
+    if x.dtype not in _DT:
+        raise TypeError("dtype must be float32 or bfloat16")
+    s = torch.empty(B, L, dtype=torch.float32, device=x.device)
+    N.check("rs_score", lib().rs_score(fx.data_ptr(), x.data_ptr(), B, L, C, _DT[x.dtype],
+                                       s.data_ptr(), _stream()))
+    return s
+
+
+def topk_gather(scores: torch.Tensor, x: Optional[torch.Tensor], keep_k: int, has_cls: bool):
+    """Per-sample top-keep_k of scores [B, L] (fp32).  Returns (kept_idx [B, keep_k] int32,
+    x_kept [B, keep_k, C] or None when x is None)."""
+    B, L = scores.shape
+    _dev(scores, "scores", torch.float32)
+    kept = torch.empty(B, keep_k, dtype=torch.int32, device=scores.device)
+    if x is not None:
+        _dev(x, "x", None, (B, L, x.shape[2]))
+        if x.dtype not in _DT:
+            raise TypeError("dtype must be float32 or bfloat16")
+        C, dt = x.shape[2], _DT[x.dtype]
+        xk = torch.empty(B, keep_k, C, dtype=x.dtype, device=x.device)
+        xp, xkp = x.data_ptr(), xk.data_ptr()
+    else:
+        C, dt, xk, xp, xkp = 0, N.RS_F32, None, None, None
+    N.check("rs_topk_gather", lib().rs_topk_gather(scores.data_ptr(), xp, B, L, C, dt, keep_k,
+                                                   int(has_cls), kept.data_ptr(), xkp, _stream()))
+    return kept, xk
+
+
+def encoder_out_len(depth: int, L: int, prune_layers: Sequence[int],
+                    keep_ratios: Sequence[float]) -> int:
+    out = ctypes.c_int(0)
+    N.check("rs_encoder_out_len", lib().rs_encoder_out_len(
+        depth, L, N.int_array(prune_layers), N.dbl_array(keep_ratios), len(prune_layers),
+        ctypes.byref(out)))
+    return out.value
+
+
+class Encoder:
+    """A whole encoder bound to fixed (B, L) with its workspace and outputs allocated
+    once, so repeated forward() calls allocate nothing."""
+
+    def __init__(self, spec: ModelSpec, blocks: List[Dict[str, torch.Tensor]], B: int, L: int,
+                 prune_layers: Sequence[int], keep_ratios: Sequence[float], device="cuda"):
+        self.spec, self.B, self.L = spec, B, L
+        self.depth = len(blocks)
+        self.prune = list(prune_layers)
+        self.ratios = [float(r) for r in keep_ratios]
+        self.L_final = encoder_out_len(self.depth, L, self.prune, self.ratios)
+        self._blocks = blocks  # keep the tensors alive
+        self._w = (N.BlockWeights * self.depth)(*[_weights(spec, w) for w in blocks])
+        self._desc = spec.desc()
+        self._pl, self._kr = N.int_array(self.prune), N.dbl_array(self.ratios)
+        self.workspace = _workspace(spec, self.depth, B, L, device)
+        self.out = torch.empty(B, self.L_final, spec.C, dtype=spec.dtype, device=device)
+        self.out_idx = torch.empty(B, self.L_final, dtype=torch.int32, device=device)
+
+    def forward(self, x: torch.Tensor):
+        _dev(x, "x", self.spec.dtype, (self.B, self.L, self.spec.C))
+        N.check("rs_encoder_forward", lib().rs_encoder_forward(
+            ctypes.byref(self._desc), self._w, self.depth, x.data_ptr(), self.B, self.L,
+            self._pl, self._kr, len(self.prune), self.out.data_ptr(), self.out_idx.data_ptr(),
+            self.workspace.data_ptr(), self.workspace.numel(), _stream()))
+        return self.out, self.out_idx
+
+
+def encoder_forward(spec: ModelSpec, blocks: List[Dict[str, torch.Tensor]], x: torch.Tensor,
+                    prune_layers: Sequence[int], keep_ratios: Sequence[float]):
+    """Whole encoder with progressive pruning.  Returns (out [B, L_final, C],
+    out_idx [B, L_final] original token ids)."""
+    B, L, _ = x.shape
+    enc = Encoder(spec, blocks, B, L, prune_layers, keep_ratios, device=x.device)
+    out, idx = enc.forward(x)
+    return out, idx
+
+
+class KernelTimer:
+    """HIP-event timing of one kernel class inside the library (see rs_timing_begin)."""
+
+    def __init__(self, kernel: str):
+        self.kid = KERNELS.index(kernel)
+
+    def __enter__(self):
+        N.check("rs_timing_begin", lib().rs_timing_begin(self.kid))
+        return self
+
+    def __exit__(self, *exc):
+        ms, n, work = ctypes.c_float(), ctypes.c_int(), ctypes.c_double()
+        st = lib().rs_timing_end(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work))
+        if exc[0] is None:
+            N.check("rs_timing_end", st)
+        self.total_ms, self.launches, self.work = ms.value, n.value, work.value
+        return False

@@ -1,0 +1,447 @@
+// Host side of the C ABI declared in include/rs.h: argument validation (complete
+// before anything is enqueued), workspace carving, the per-block launch sequence, the
+// encoder's pruning schedule, and optional per-kernel event timing.
+//
+// The schedule follows "Representation Shift: Unifying Token Compression with
+// FlashAttention" (arXiv HTML): tokens are pruned after the listed blocks, each time
+// keeping a fraction of the *current* tokens (Sec. 4.1 and 4.2 settings); the kept count
+// is floor(r*L + 1/2) evaluated in IEEE double.  This file is compiled with
+// -ffp-contract=off so that r*L + 1/2 is two correctly rounded operations.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rs.h"
+#include "rs_launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+rs_status fail(rs_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t esize(rs_dtype dt) { return dt == RS_BF16 ? 2 : 4; }
+size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------------ kernel timing
+std::atomic<int> g_timed_kernel{-1};
+std::mutex g_tmu;
+std::vector<hipEvent_t> g_ev;  // start/end pairs, reused across sessions
+size_t g_ev_used = 0;
+double g_work = 0.0;
+hipError_t g_timing_err = hipSuccess;
+
+template <class F>
+hipError_t timed(int kid, double work, hipStream_t st, F&& launch) {
+  if (g_timed_kernel.load(std::memory_order_relaxed) != kid) return launch();
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_ev_used + 2 > g_ev.size()) {
+    for (int i = 0; i < 2; ++i) {
+      hipEvent_t e;
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) {
+        g_timing_err = err;
+        return launch();
+      }
+      g_ev.push_back(e);
+    }
+  }
+  hipEvent_t a = g_ev[g_ev_used], b = g_ev[g_ev_used + 1];
+  hipError_t e1 = hipEventRecord(a, st);
+  hipError_t err = launch();
+  hipError_t e2 = hipEventRecord(b, st);
+  if (e1 != hipSuccess || e2 != hipSuccess) g_timing_err = e1 != hipSuccess ? e1 : e2;
+  g_ev_used += 2;
+  g_work += work;
+  return err;
+}
+
+// ------------------------------------------------------------------ validation
+rs_status check_desc(const rs_model_desc* d) {
+  if (!d) return fail(RS_ERR_INVALID_ARG, "desc is null");
+  if (d->dtype != RS_F32 && d->dtype != RS_BF16) return fail(RS_ERR_INVALID_ARG, "unknown dtype");
+  if (d->C <= 0 || d->heads <= 0 || d->hidden <= 0)
+    return fail(RS_ERR_INVALID_ARG, "C, heads and hidden must be positive");
+  if (d->C % 64 != 0 || d->heads * 64 != d->C)
+    return fail(RS_ERR_UNSUPPORTED, "head dim must be 64 (C == heads*64, C % 64 == 0)");
+  if (d->C > 1024) return fail(RS_ERR_UNSUPPORTED, "C > 1024");
+  if (d->hidden % 64 != 0) return fail(RS_ERR_UNSUPPORTED, "hidden % 64 != 0");
+  if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps)) return fail(RS_ERR_INVALID_ARG, "ln_eps must be > 0");
+  if (d->has_cls != 0 && d->has_cls != 1) return fail(RS_ERR_INVALID_ARG, "has_cls must be 0 or 1");
+  return RS_OK;
+}
+
+rs_status check_BL(int B, int L, int C, int wide) {
+  if (B < 1 || L < 1) return fail(RS_ERR_INVALID_ARG, "B and L must be >= 1");
+  if (L > RS_MAX_TOKENS) return fail(RS_ERR_UNSUPPORTED, "L > RS_MAX_TOKENS");
+  const long long M = (long long)B * L;
+  if (M * (long long)(wide > C ? wide : C) >= (1LL << 31))
+    return fail(RS_ERR_UNSUPPORTED, "B*L*width must stay below 2^31");
+  return RS_OK;
+}
+
+rs_status check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(RS_ERR_INVALID_ARG, std::string(name) + " is null");
+  if (!aligned(p, align))
+    return fail(RS_ERR_INVALID_ARG, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return RS_OK;
+}
+
+rs_status check_weights(const rs_block_weights* w) {
+  if (!w) return fail(RS_ERR_INVALID_ARG, "weights are null");
+  const void* ps[12] = {w->ln1_g, w->ln1_b, w->w_qkv, w->b_qkv, w->w_proj, w->b_proj,
+                        w->ln2_g, w->ln2_b, w->w_fc1, w->b_fc1, w->w_fc2, w->b_fc2};
+  static const char* names[12] = {"ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj",
+                                  "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2"};
+  for (int i = 0; i < 12; ++i) {
+    rs_status s = check_ptr(ps[i], names[i]);
+    if (s != RS_OK) return s;
+  }
+  return RS_OK;
+}
+
+// kept count at a prune block: floor(r * L + 1/2), both steps rounded in double
+bool keep_count(double r, int L, int* k) {
+  if (!(r > 0.0) || !(r <= 1.0)) return false;
+  const double prod = r * (double)L;
+  const double kk = floor(prod + 0.5);
+  if (kk < 1.0 || kk > (double)L) return false;
+  *k = (int)kk;
+  return true;
+}
+
+rs_status check_schedule(int depth, int L, const int* prune, const double* ratios, int n,
+                         int* L_final, std::vector<int>* ks) {
+  if (depth < 1) return fail(RS_ERR_INVALID_ARG, "depth must be >= 1");
+  if (n < 0) return fail(RS_ERR_INVALID_ARG, "n_prune < 0");
+  if (n > 0 && (!prune || !ratios)) return fail(RS_ERR_INVALID_ARG, "prune_layers/keep_ratios null");
+  int cur = L;
+  for (int i = 0; i < n; ++i) {
+    if (prune[i] < 0 || prune[i] >= depth)
+      return fail(RS_ERR_INVALID_ARG, "prune layer outside [0, depth)");
+    if (i > 0 && prune[i] <= prune[i - 1])
+      return fail(RS_ERR_INVALID_ARG, "prune_layers must be strictly ascending");
+    int k;
+    if (!keep_count(ratios[i], cur, &k))
+      return fail(RS_ERR_INVALID_ARG, "keep ratio must be in (0, 1] and keep >= 1 token");
+    if (ks) ks->push_back(k);
+    cur = k;
+  }
+  *L_final = cur;
+  return RS_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+struct BlockWs {
+  void *xn, *qk, *vt, *o, *p, *h, *xhat;
+  float* part;
+};
+
+// Carves the per-block buffers for (B, L) from `base` (or only sizes them if null).
+size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws) {
+  const size_t e = esize(d.dtype), M = (size_t)B * L, C = d.C;
+  const size_t sizes[8] = {
+      up256(M * C * e),                                  // xn: LN output
+      up256(M * 2 * C * e),                              // qk: Q | K
+      up256((size_t)B * d.heads * 64 * rs::padded_len(L) * e),  // vt: V^T per head
+      up256(M * C * e),                                  // o: attention output
+      up256(M * C * e),                                  // p: attention branch (proj out)
+      up256(M * (size_t)d.hidden * e),                   // h: GELU(fc1)
+      up256(M * C * e),                                  // xhat: block output
+      up256(M * (size_t)rs::score_parts(d.C) * 4),       // part: score partials
+  };
+  size_t off = 0;
+  void* ptrs[8];
+  for (int i = 0; i < 8; ++i) {
+    ptrs[i] = base ? base + off : nullptr;
+    off += sizes[i];
+  }
+  if (ws) {
+    ws->xn = ptrs[0]; ws->qk = ptrs[1]; ws->vt = ptrs[2]; ws->o = ptrs[3];
+    ws->p = ptrs[4]; ws->h = ptrs[5]; ws->xhat = ptrs[6];
+    ws->part = static_cast<float*>(ptrs[7]);
+  }
+  return off;
+}
+
+struct EncWs {
+  BlockWs blk;
+  void* act;      // [B][L][C] running activations
+  int32_t* kept;  // [B][L]
+  int32_t* ids[2];
+};
+
+size_t carve_encoder(const rs_model_desc& d, int B, int L, char* base, EncWs* ws) {
+  size_t off = carve_block(d, B, L, base, ws ? &ws->blk : nullptr);
+  const size_t act = up256((size_t)B * L * d.C * esize(d.dtype));
+  const size_t idb = up256((size_t)B * L * 4);
+  if (ws) {
+    ws->act = base + off;
+    ws->kept = reinterpret_cast<int32_t*>(base + off + act);
+    ws->ids[0] = reinterpret_cast<int32_t*>(base + off + act + idb);
+    ws->ids[1] = reinterpret_cast<int32_t*>(base + off + act + 2 * idb);
+  }
+  return off + act + 3 * idb;
+}
+
+// ------------------------------------------------------------------ launch sequence
+#define RS_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) return fail(RS_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// One block: Eq. (5) then Eq. (6); the fc2 epilogue writes x_hat to `out` and, if
+// `part` is not null, the per-token partial sums of the squared MLP-sublayer shift.
+// `out` may alias `x` (the fc2 epilogue reads each element of x before it writes it,
+// and nothing reads x after that).
+rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const void* x, int B, int L,
+                    void* out, float* part, const BlockWs& ws, hipStream_t st) {
+  const rs::Dtype dt = d.dtype == RS_BF16 ? rs::kBF16 : rs::kF32;
+  const int M = B * L, C = d.C, Hd = d.hidden;
+  const double e = (double)esize(d.dtype);
+  const double Md = M, Cd = C;
+
+  RS_HIP(timed(RS_KERNEL_LAYERNORM, Md * Cd * e * 2, st, [&] {
+    return rs::launch_layernorm(dt, x, nullptr, w.ln1_g, w.ln1_b, d.ln_eps, ws.xn, M, C, st);
+  }));
+  {
+    rs::GemmEpiArgs ep;
+    ep.bias = w.b_qkv; ep.out = ws.qk; ep.ldo = 2 * C;
+    ep.vt = ws.vt; ep.vcol0 = 2 * C; ep.L = L; ep.Lp = rs::padded_len(L); ep.heads = d.heads;
+    RS_HIP(timed(RS_KERNEL_QKV, 2.0 * Md * 3 * Cd * Cd, st, [&] {
+      return rs::launch_gemm(dt, rs::kEpiQKV, ws.xn, w.w_qkv, M, 3 * C, C, ep, st);
+    }));
+  }
+  RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
+    return rs::launch_attention(dt, ws.qk, ws.vt, ws.o, B, L, d.heads, rs::padded_len(L), st);
+  }));
+  {
+    rs::GemmEpiArgs ep;
+    ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
+    RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
+      return rs::launch_gemm(dt, rs::kEpiBias, ws.o, w.w_proj, M, C, C, ep, st);
+    }));
+  }
+  RS_HIP(timed(RS_KERNEL_LAYERNORM, Md * Cd * e * 3, st, [&] {
+    return rs::launch_layernorm(dt, x, ws.p, w.ln2_g, w.ln2_b, d.ln_eps, ws.xn, M, C, st);
+  }));
+  {
+    rs::GemmEpiArgs ep;
+    ep.bias = w.b_fc1; ep.out = ws.h; ep.ldo = Hd;
+    RS_HIP(timed(RS_KERNEL_FC1, 2.0 * Md * Cd * Hd, st, [&] {
+      return rs::launch_gemm(dt, rs::kEpiGelu, ws.xn, w.w_fc1, M, Hd, C, ep, st);
+    }));
+  }
+  {
+    rs::GemmEpiArgs ep;
+    ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
+    ep.x = x; ep.p = ws.p; ep.part = part; ep.nparts = rs::score_parts(C);
+    RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
+      return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
+    }));
+  }
+  return RS_OK;
+}
+
+rs_status run_select(int B, int L, int k, int has_cls, const float* scores, const float* part,
+                     int P, float* scores_out, int32_t* kept, const int32_t* ids_in,
+                     int32_t* ids_out, const void* x, void* x_kept, size_t row_bytes,
+                     hipStream_t st) {
+  const double topk_bytes = (double)B * L * 4.0 * (part ? P : 1) + (scores_out ? B * L * 4.0 : 0.0) +
+                            (double)B * k * 4.0 * (ids_out ? 2 : 1);
+  RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes, st, [&] {
+    return rs::launch_topk(scores, part, P, B, L, k, has_cls, scores_out, kept, ids_in, ids_out, st);
+  }));
+  if (x_kept) {
+    RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)row_bytes + B * k * 4.0, st, [&] {
+      return rs::launch_gather(x, kept, x_kept, B, L, k, (int)row_bytes, st);
+    }));
+  }
+  return RS_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* rs_last_error(void) { return g_err.c_str(); }
+
+size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L) {
+  std::string saved = g_err;
+  if (check_desc(desc) != RS_OK || depth < 1 || B < 1 || L < 1) {
+    g_err = saved;
+    return 0;
+  }
+  // one size serves both entry points: the encoder's carve contains the block's
+  return carve_encoder(*desc, B, L, nullptr, nullptr);
+}
+
+rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers, const double* keep_ratios,
+                             int n_prune, int* L_final) {
+  if (!L_final) return fail(RS_ERR_INVALID_ARG, "L_final is null");
+  if (L < 1) return fail(RS_ERR_INVALID_ARG, "L must be >= 1");
+  return check_schedule(depth, L, prune_layers, keep_ratios, n_prune, L_final, nullptr);
+}
+
+rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w, const void* x,
+                           int B, int L, int keep_k, void* y, float* scores, int32_t* kept_idx,
+                           void* y_kept, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  if ((s = check_weights(w)) != RS_OK) return s;
+  if ((s = check_BL(B, L, desc->C, desc->hidden > 3 * desc->C ? desc->hidden : 3 * desc->C)) != RS_OK) return s;
+  if (keep_k < 1 || keep_k > L) return fail(RS_ERR_INVALID_ARG, "keep_k outside [1, L]");
+  if ((s = check_ptr(x, "x")) != RS_OK) return s;
+  if (y && (s = check_ptr(y, "y")) != RS_OK) return s;
+  if (scores && (s = check_ptr(scores, "scores")) != RS_OK) return s;
+  if ((s = check_ptr(kept_idx, "kept_idx")) != RS_OK) return s;
+  if ((s = check_ptr(y_kept, "y_kept")) != RS_OK) return s;
+  if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+  const size_t need = carve_block(*desc, B, L, nullptr, nullptr);
+  if (ws_bytes < need)
+    return fail(RS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+
+  BlockWs ws;
+  carve_block(*desc, B, L, static_cast<char*>(workspace), &ws);
+  void* xhat = y ? y : ws.xhat;
+  if ((s = run_block(*desc, *w, x, B, L, xhat, ws.part, ws, stream)) != RS_OK) return s;
+  return run_select(B, L, keep_k, desc->has_cls, nullptr, ws.part, rs::score_parts(desc->C), scores,
+                    kept_idx, nullptr, nullptr, xhat, y_kept, (size_t)desc->C * esize(desc->dtype),
+                    stream);
+}
+
+rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype, float* scores,
+                   hipStream_t stream) {
+  rs_status s;
+  if (dtype != RS_F32 && dtype != RS_BF16) return fail(RS_ERR_INVALID_ARG, "unknown dtype");
+  if (C < 8 || C % 8 != 0) return fail(RS_ERR_UNSUPPORTED, "C must be a positive multiple of 8");
+  if ((s = check_BL(B, L, C, C)) != RS_OK) return s;
+  if ((s = check_ptr(fx, "fx")) != RS_OK) return s;
+  if ((s = check_ptr(x, "x")) != RS_OK) return s;
+  if ((s = check_ptr(scores, "scores")) != RS_OK) return s;
+  const int M = B * L;
+  RS_HIP(timed(RS_KERNEL_SCORE, (double)M * C * esize(dtype) * 2 + M * 4.0, stream, [&] {
+    return rs::launch_score_rows(dtype == RS_BF16 ? rs::kBF16 : rs::kF32, fx, x, scores, M, C, stream);
+  }));
+  return RS_OK;
+}
+
+rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C, rs_dtype dtype,
+                         int keep_k, int has_cls, int32_t* kept_idx, void* x_kept,
+                         hipStream_t stream) {
+  rs_status s;
+  if (dtype != RS_F32 && dtype != RS_BF16) return fail(RS_ERR_INVALID_ARG, "unknown dtype");
+  if (has_cls != 0 && has_cls != 1) return fail(RS_ERR_INVALID_ARG, "has_cls must be 0 or 1");
+  if (x_kept && (C < 1 || (C * esize(dtype)) % 16 != 0))
+    return fail(RS_ERR_UNSUPPORTED, "row bytes must be a multiple of 16");
+  if ((s = check_BL(B, L, C > 0 ? C : 1, C > 0 ? C : 1)) != RS_OK) return s;
+  if (keep_k < 1 || keep_k > L) return fail(RS_ERR_INVALID_ARG, "keep_k outside [1, L]");
+  if ((s = check_ptr(scores, "scores", 4)) != RS_OK) return s;
+  if ((s = check_ptr(kept_idx, "kept_idx", 4)) != RS_OK) return s;
+  if (x_kept) {
+    if ((s = check_ptr(x, "x")) != RS_OK) return s;
+    if ((s = check_ptr(x_kept, "x_kept")) != RS_OK) return s;
+  }
+  return run_select(B, L, keep_k, has_cls, scores, nullptr, 0, nullptr, kept_idx, nullptr, nullptr, x,
+                    x_kept, (size_t)C * esize(dtype), stream);
+}
+
+rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* blocks, int depth,
+                             const void* x, int B, int L, const int* prune_layers,
+                             const double* keep_ratios, int n_prune, void* out, int32_t* out_idx,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  if (!blocks) return fail(RS_ERR_INVALID_ARG, "blocks is null");
+  if ((s = check_BL(B, L, desc->C, desc->hidden > 3 * desc->C ? desc->hidden : 3 * desc->C)) != RS_OK) return s;
+  int L_final = 0;
+  std::vector<int> ks;
+  if ((s = check_schedule(depth, L, prune_layers, keep_ratios, n_prune, &L_final, &ks)) != RS_OK) return s;
+  for (int b = 0; b < depth; ++b)
+    if ((s = check_weights(&blocks[b])) != RS_OK)
+      return fail(s, "block " + std::to_string(b) + ": " + g_err);
+  if ((s = check_ptr(x, "x")) != RS_OK) return s;
+  if ((s = check_ptr(out, "out")) != RS_OK) return s;
+  if ((s = check_ptr(out_idx, "out_idx", 4)) != RS_OK) return s;
+  if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+  const size_t need = carve_encoder(*desc, B, L, nullptr, nullptr);
+  if (ws_bytes < need)
+    return fail(RS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+
+  EncWs ws;
+  carve_encoder(*desc, B, L, static_cast<char*>(workspace), &ws);
+  const size_t row_bytes = (size_t)desc->C * esize(desc->dtype);
+  const int P = rs::score_parts(desc->C);
+  const void* cur = x;  // block input
+  int curL = L, pi = 0;
+  const int32_t* ids = nullptr;  // original ids of the current rows (null = identity)
+  for (int b = 0; b < depth; ++b) {
+    const bool prune = pi < n_prune && prune_layers[pi] == b;
+    const bool last = b == depth - 1;
+    if (!prune) {
+      void* dst = last ? out : ws.act;
+      if ((s = run_block(*desc, blocks[b], cur, B, curL, dst, nullptr, ws.blk, stream)) != RS_OK) return s;
+      cur = dst;
+      continue;
+    }
+    const int k = ks[pi];
+    const bool last_prune = pi == n_prune - 1;
+    int32_t* ids_out = last_prune ? out_idx : ws.ids[pi & 1];
+    void* dst = last ? out : ws.act;
+    if ((s = run_block(*desc, blocks[b], cur, B, curL, ws.blk.xhat, ws.blk.part, ws.blk, stream)) != RS_OK)
+      return s;
+    if ((s = run_select(B, curL, k, desc->has_cls, nullptr, ws.blk.part, P, nullptr, ws.kept, ids,
+                        ids_out, ws.blk.xhat, dst, row_bytes, stream)) != RS_OK)
+      return s;
+    cur = dst;
+    ids = ids_out;
+    curL = k;
+    ++pi;
+  }
+  if (n_prune == 0) RS_HIP(rs::launch_iota(out_idx, B, L, stream));
+  return RS_OK;
+}
+
+rs_status rs_timing_begin(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= RS_KERNEL_COUNT) return fail(RS_ERR_INVALID_ARG, "bad kernel id");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_timed_kernel.load() != -1) return fail(RS_ERR_INVALID_ARG, "a timing session is open");
+  g_ev_used = 0;
+  g_work = 0.0;
+  g_timing_err = hipSuccess;
+  g_timed_kernel.store(kernel_id);
+  return RS_OK;
+}
+
+rs_status rs_timing_end(float* total_ms, int* launches, double* work) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_timed_kernel.load() == -1) return fail(RS_ERR_INVALID_ARG, "no timing session is open");
+  g_timed_kernel.store(-1);
+  if (g_timing_err != hipSuccess)
+    return fail(RS_ERR_HIP, std::string("timing event: ") + hipGetErrorString(g_timing_err));
+  float sum = 0.f;
+  for (size_t i = 0; i + 1 < g_ev_used; i += 2) {
+    hipError_t e = hipEventSynchronize(g_ev[i + 1]);
+    if (e != hipSuccess) return fail(RS_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_ev[i], g_ev[i + 1]);
+    if (e != hipSuccess) return fail(RS_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int)(g_ev_used / 2);
+  if (work) *work = g_work;
+  return RS_OK;
+}
+
+}  // extern "C"

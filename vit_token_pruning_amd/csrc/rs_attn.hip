@@ -1,0 +1,225 @@
+// Fused multi-head attention that never stores the attention map: Eq. (1) of
+// "Representation Shift: Unifying Token Compression with FlashAttention" (arXiv HTML,
+// Sec. 3.1), Softmax(Q K^T / sqrt(d)) V per head with d = 64, computed one 64-key
+// block at a time with a running maximum and running denominator (the softmax
+// rescaling identity; Sec. 1 explains why fused kernels such as FlashAttention are the
+// setting the method targets: no L x L map is written to HBM).
+//
+// gfx950 mapping
+//  - one workgroup = (sample, head, 64 queries); 4 waves, 16 queries each.
+//  - the scores are computed transposed, S^T = K Q^T (keys on MFMA rows, queries on
+//    columns), so each lane owns one query: its row max / row sum need no cross-lane
+//    work inside a tile beyond the 4 lane groups, the rescale factor applies to the
+//    lane's own output registers, and the probabilities are already in the register
+//    layout the P V product wants as its B operand (no LDS round trip for P).
+//  - K tiles [64 keys][64 d] and V^T tiles [64 d][64 keys] are staged in LDS, double
+//    buffered; V^T comes pre-transposed from the QKV epilogue, so both products read
+//    K-contiguous fragments.
+//  - exp2 with log2(e)/sqrt(d) folded into one FMA per score.
+#include "rs_device.hpp"
+#include "rs_launch.hpp"
+
+namespace rs {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void mask_tail(Frag8<T>& f, int nvalid) {
+  // zero elements nvalid..7 of the fragment (keys past the sequence end)
+  T* e = reinterpret_cast<T*>(&f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i >= nvalid) e[i] = from_f32<T>(0.f);
+}
+
+// The 8 k-slots of P^T for lane group g and 32-key chunk kc hold keys
+// {32kc + 4g + v} (slots 0..3, from score tile 2kc) and {32kc + 16 + 4g + v} (slots 4..7,
+// from score tile 2kc+1).  The V^T fragment below uses the same assignment.
+__device__ __forceinline__ void pack_p(Frag8<bf16>& f, const f32x4& a, const f32x4& b) {
+  f.v[0] = pack_bf16x2(a[0], a[1]);
+  f.v[1] = pack_bf16x2(a[2], a[3]);
+  f.v[2] = pack_bf16x2(b[0], b[1]);
+  f.v[3] = pack_bf16x2(b[2], b[3]);
+}
+__device__ __forceinline__ void pack_p(Frag8<float>& f, const f32x4& a, const f32x4& b) {
+  f.v[0] = __builtin_bit_cast(u32x4, a);
+  f.v[1] = __builtin_bit_cast(u32x4, b);
+}
+__device__ __forceinline__ void load_vt(Frag8<bf16>& f, const char* lo, const char* hi) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(lo);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(hi);
+  f.v = u32x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ void load_vt(Frag8<float>& f, const char* lo, const char* hi) {
+  f.v[0] = *reinterpret_cast<const u32x4*>(lo);
+  f.v[1] = *reinterpret_cast<const u32x4*>(hi);
+}
+__device__ __forceinline__ void store_o4(bf16* p, const f32x4& o, float s) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0] * s, o[1] * s), pack_bf16x2(o[2] * s, o[3] * s)};
+}
+__device__ __forceinline__ void store_o4(float* p, const f32x4& o, float s) {
+  *reinterpret_cast<f32x4*>(p) = o * s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk,
+                                                        const T* __restrict__ vt,
+                                                        T* __restrict__ out, int L, int H, int Lp,
+                                                        float scale_log2) {
+  constexpr int CB = Chunk<T>::bytes;  // 8 elements
+  constexpr int ROWB = 8 * CB;         // 64 elements
+  constexpr int TB = 64 * ROWB;        // one 64 x 64 tile
+  __shared__ __attribute__((aligned(16))) char smem[4 * TB];
+
+  const int C = H * 64, ldqk = 2 * C;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int q0 = blockIdx.x * 64 + wave * 16;
+  const size_t row0 = (size_t)b * L;
+
+  // Q as the B operand: lane (g, l16) holds query q0+l16, d = 32ks + 8g .. +7
+  Frag8<T> qf[2];
+  {
+    const int q = min(q0 + l16, L - 1);
+    const T* qp = qk + (row0 + q) * ldqk + h * 64 + g * 8;
+    load_frag(qf[0], qp);
+    load_frag(qf[1], qp + 32);
+  }
+
+  // staging: 2 chunks of K rows and 2 chunks of V^T rows per thread per tile
+  const int lc = tid & 7, lr = tid >> 3;
+  const T* kbase = qk + row0 * ldqk + C + h * 64 + lc * 8;
+  const T* vbase = vt + (size_t)(b * H + h) * 64 * Lp + lc * 8;
+  Frag8<T> rk[2], rv[2];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = lr + 32 * i;
+      const int key = min(kt * 64 + r, L - 1);
+      load_frag(rk[i], kbase + (size_t)key * ldqk);
+      load_frag(rv[i], vbase + (size_t)r * Lp + kt * 64);
+      const int nv = L - (kt * 64 + lc * 8);
+      if (nv < 8) mask_tail(rv[i], nv < 0 ? 0 : nv);
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* Ks = smem + buf * 2 * TB;
+    char* Vs = Ks + TB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = lr + 32 * i;
+      const int off = r * ROWB + ((lc ^ (r & 7)) * CB);
+      store_frag(Ks + off, rk[i]);
+      store_frag(Vs + off, rv[i]);
+    }
+  };
+
+  f32x4 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int nk = (L + 63) / 64;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    const char* Ks = smem + (kt & 1) * 2 * TB;
+    const char* Vs = Ks + TB;
+
+    // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
+    f32x4 s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = j * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + g;
+        Frag8<T> kf;
+        load_frag(kf, Ks + r * ROWB + ((c ^ (r & 7)) * CB));
+        s[j] = mma16(s[j], kf, qf[ks]);
+      }
+    }
+    if (kt * 64 + 64 > L) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kt * 64 + j * 16 + 4 * g + v >= L) s[j][v] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f((m_run - m_new) * scale_log2);
+    const float mb = m_new * scale_log2;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = exp2f(fmaf(s[j][v], scale_log2, -mb));
+        s[j][v] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+
+    Frag8<T> pf[2];
+    pack_p(pf[0], s[0], s[1]);
+    pack_p(pf[1], s[2], s[3]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = d * 16 + l16;
+      const char* vrow = Vs + r * ROWB;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int ca = 4 * kc + (g >> 1), cb = ca + 2;
+        const int half = (g & 1) * (CB / 2);
+        Frag8<T> vf;
+        load_vt(vf, vrow + ((ca ^ (r & 7)) * CB) + half, vrow + ((cb ^ (r & 7)) * CB) + half);
+        o[d] = mma16(o[d], vf, pf[kc]);
+      }
+    }
+    if (more) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  float lt = l_run + __shfl_xor(l_run, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  const float inv = 1.0f / lt;
+  const int q = q0 + l16;
+  if (q < L) {
+    T* op = out + (row0 + q) * C + h * 64 + 4 * g;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) store_o4(op + d * 16, o[d], inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(Dtype dt, const void* qk, const void* vt, void* out, int B, int L,
+                            int H, int Lp, hipStream_t stream) {
+  const dim3 grid((L + 63) / 64, H, B);
+  const float scale_log2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+  if (dt == kBF16)
+    attention_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(qk),
+                                                     static_cast<const bf16*>(vt),
+                                                     static_cast<bf16*>(out), L, H, Lp, scale_log2);
+  else
+    attention_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(qk),
+                                                      static_cast<const float*>(vt),
+                                                      static_cast<float*>(out), L, H, Lp, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace rs
