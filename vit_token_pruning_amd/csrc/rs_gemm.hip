@@ -1,233 +1,300 @@
 // Tile GEMM Y = A W^T on the gfx950 matrix cores with the block's fused epilogues:
-// QKV (bias, per-head transposed V), attention projection (bias), fc1 (bias + exact
-// GELU) and fc2 (bias, residual re-formed in fp32, and the per-token partial sums of
-// squares of the MLP-sublayer representation shift).
+// QKV (bias, per-head transposed V), attention projection (bias), fc1 (bias + GELU)
+// and fc2 (bias, residual re-formed in fp32, and the per-token partial sums of squares
+// of the MLP-sublayer representation shift).
 //
 // The score is Eq. (4) of "Representation Shift: Unifying Token Compression with
 // FlashAttention" (arXiv HTML), Sec. 3.2, for the MLP sublayer of Sec. 3.3 (case ii)
-// and the L2 distance: || MLP(LN(x')) - x' ||_2.  The fc2 accumulators already hold
-// MLP(LN(x')) - b2 in fp32, so the squared difference is summed while the tile is in
-// registers/LDS and the MLP output is never re-read from HBM.
+// and the L2 distance: || MLP(LN(x')) - x' ||_2.  The fc2 accumulators hold
+// MLP(LN(x')) - b2 in fp32; the squared difference to x' is summed in registers while
+// the output is written, so the MLP output is never re-read from HBM.
 //
 // Layout: A [M][K] (activations), W [N][K] (Linear weight, [out][in]); both are
-// K-contiguous.  Workgroup tile 128 (M) x 128 (N), 4 waves in 2 x 2, each 64 x 64 as
-// 4 x 4 MFMA 16x16x32 tiles.  K advances 64 (bf16) or 32 (fp32) per LDS stage, double
-// buffered: the next stage's global loads are in flight while the current one is
-// multiplied.  LDS rows hold 8 chunks of 8 elements; chunk c of row r sits at slot
-// c ^ (r % chunks) so the 16 rows a fragment read touches land on distinct banks.
+// K-contiguous.  A workgroup of WM x WN waves computes a (WM*TM*16) x (WN*TN*16) tile,
+// each wave TM x TN MFMA 16x16x32 tiles.  K advances 64 (bf16) or 32 (fp32) elements
+// per LDS stage; LDS is double buffered and global loads run PF stages ahead through
+// registers, so a stage's loads have PF-1 whole stages of matrix work to land behind.
+// LDS rows hold 8 chunks of 8 elements; chunk c of row r sits at slot c ^ (r % chunks)
+// so the 16 rows of a fragment read fall on distinct banks.
+//
+// Orientation: the weight fragment is the MFMA A operand and the activation fragment
+// the B operand, so a lane ends up holding 4 consecutive output columns of one row.
+// The epilogue stages the fp32 tile in LDS -- row-major for the row-wise epilogues
+// (bias, GELU, residual, score), transposed for the V columns of the QKV projection,
+// whose output is V^T per head -- so every global access is a row-contiguous line.
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
 
 namespace rs {
 namespace {
 
-constexpr int BM = kGemmTile, BN = kGemmTile;
-constexpr int CS = BN + 4;  // fp32 row stride of the staged output tile
+// GELU for bf16 outputs: x * Phi(x) with Phi(x) = logistic(t * P(t^2)), t = clamp(x, +-6),
+// P a degree-3 polynomial in t^2 fitted (weighted minimax) to the logit of the normal
+// CDF, log2(e) folded in so the logistic is 1 / (1 + 2^-(t P)).  Max |error| against the
+// exact erf form over all x: 1.3e-5 (about 1/150 of a bf16 half-ulp at 1).
+__device__ __forceinline__ float gelu_fitted(float x) {
+  const float t = __builtin_amdgcn_fmed3f(x, -6.0f, 6.0f);
+  const float u = t * t;
+  float p = fmaf(u, -2.4996252250275575e-05f, -7.343353936448693e-04f);
+  p = fmaf(p, u, 1.059778556227684e-01f);
+  p = fmaf(p, u, 2.3016505241394043f);
+  const float e = __builtin_amdgcn_exp2f(-(t * p));
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+template <typename T> __device__ __forceinline__ float gelu_t(float x);
+template <> __device__ __forceinline__ float gelu_t<bf16>(float x) { return gelu_fitted(x); }
+template <> __device__ __forceinline__ float gelu_t<float>(float x) { return gelu_erf(x); }
 
-template <typename T> struct GemmShape {
-  static constexpr int KC = sizeof(T) == 2 ? 8 : 4;  // chunks per row per stage
-  static constexpr int CB = Chunk<T>::bytes;           // chunk bytes
+constexpr int kCS = kGemmTile + 4;  // fp32 row stride of the staged output tile
+
+template <typename T, int WM_, int WN_, int TM_, int TN_, int PF_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, PF = PF_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
+  static constexpr int KC = sizeof(T) == 2 ? 8 : 4;   // 8-element chunks per row per stage
+  static constexpr int CB = Chunk<T>::bytes;
   static constexpr int ROWB = KC * CB;                 // 128 bytes per tile row
-  static constexpr int OPB = BM * ROWB;                // one operand tile: 16 KB
-  static constexpr int SMEM = (4 * OPB > BM * CS * 4) ? 4 * OPB : BM * CS * 4;
+  static constexpr int ABYTES = BM * ROWB;
+  static constexpr int STAGE = (BM + BN) * ROWB;
+  static constexpr int NA = BM * KC / NT, NW = BN * KC / NT;
+  static constexpr int RSTEP = NT / KC;
+  static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "loader must divide evenly");
 };
 
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const T* __restrict__ A,
-                                                      const T* __restrict__ W, int M, int N,
-                                                      int K, GemmEpiArgs ep) {
-  using S = GemmShape<T>;
-  constexpr int KC = S::KC, CB = S::CB, ROWB = S::ROWB, OPB = S::OPB;
-  __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
+template <typename T, int EPI, class G>
+__global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
+                                                     const T* __restrict__ W, int M, int N,
+                                                     int K, GemmEpiArgs ep) {
+  constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
+  constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
+  constexpr int SMEM = 2 * STAGE > G::BM * kCS * 4 ? 2 * STAGE : G::BM * kCS * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
+  const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
   const int t = xcd_contiguous(blockIdx.x, nM * nN);
   const int mt = t / nN, nt = t - mt * nN;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = mt * G::BM, n0 = nt * G::BN;
+  const int wm = wave % G::WM, wn = wave / G::WM;
 
-  // ---- global -> LDS staging: each thread moves NL chunks of A and of W per stage
-  constexpr int NL = KC / 2;
-  constexpr int RSTEP = 256 / KC;
+  // ---- loader: this thread's chunks of A and W, and their swizzled LDS slots
   const int lc = tid % KC, lr = tid / KC;
-  const char* ag[NL];
-  const char* wg[NL];
-  int so[NL];
+  const char* ag[NA];
+  const char* wg[NW];
+  int sa[NA], sw[NW];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
+  for (int i = 0; i < NA; ++i) {
     const int r = lr + i * RSTEP;
-    const int am = min(m0 + r, M - 1), wn_ = min(n0 + r, N - 1);
-    ag[i] = reinterpret_cast<const char*>(A + (size_t)am * K) + lc * CB;
-    wg[i] = reinterpret_cast<const char*>(W + (size_t)wn_ * K) + lc * CB;
-    so[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
-  }
-  Frag8<T> ra[NL], rw[NL];
-  const int KT = K / (8 * KC);
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    load_frag(ra[i], ag[i]);
-    load_frag(rw[i], wg[i]);
+    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + lc * CB;
+    sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
   }
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    store_frag(smem + so[i], ra[i]);
-    store_frag(smem + OPB + so[i], rw[i]);
+  for (int i = 0; i < NW; ++i) {
+    const int r = lr + i * RSTEP;
+    wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + lc * CB;
+    sw[i] = ABYTES + r * ROWB + ((lc ^ (r % KC)) * CB);
   }
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const size_t off = (size_t)(kt + 1) * ROWB;
+  Frag8<T> ra[PF][NA], rw[PF][NW];
+  auto gload = [&](int kt, int slot) {
+    const size_t off = (size_t)kt * ROWB;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        load_frag(ra[i], ag[i] + off);
-        load_frag(rw[i], wg[i] + off);
-      }
-    }
-    const char* As = smem + (kt & 1) * 2 * OPB;
-    const char* Ws = As + OPB;
+    for (int i = 0; i < NA; ++i) load_frag(ra[slot][i], ag[i] + off);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) load_frag(rw[slot][i], wg[i] + off);
+  };
+  auto sstore = [&](int slot, int buf) {
+    char* s = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) store_frag(s + sa[i], ra[slot][i]);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) store_frag(s + sw[i], rw[slot][i]);
+  };
+
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    const char* As = smem + buf * STAGE;
+    const char* Ws = As + ABYTES;
 #pragma unroll
     for (int ks = 0; ks < KC / 4; ++ks) {
       const int c = ks * 4 + g;
-      Frag8<T> fa[4], fw[4];
+      Frag8<T> fa[TM], fw[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + l16;
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 16 + i * 16 + l16;
         load_frag(fa[i], As + r * ROWB + ((c ^ (r % KC)) * CB));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + j * 16 + l16;
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 16 + j * 16 + l16;
         load_frag(fw[j], Ws + r * ROWB + ((c ^ (r % KC)) * CB));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = mma16(acc[j][i], fw[j], fa[i]);
+        for (int i = 0; i < TM; ++i)
+          acc[j][i] = mma16(acc[j][i], fw[j], fa[i]);
     }
-    if (more) {
-      char* Ad = smem + ((kt + 1) & 1) * 2 * OPB;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        store_frag(Ad + so[i], ra[i]);
-        store_frag(Ad + OPB + so[i], rw[i]);
-      }
-    }
+  };
+
+  const int KT = K / (8 * KC);
+  {
+    gload(0, 0);
+    sstore(0, 0);
+    if (PF > 1 && KT > 1) gload(1, 1 % PF);
     __syncthreads();
+    // One stage.  PF == 2: the next stage's registers arrived during the previous stage,
+    // so they are written to the free LDS buffer first and those writes overlap this
+    // stage's matrix work; then loads two stages ahead are issued.  PF == 1: loads one
+    // stage ahead, written to LDS after the matrix work.
+    auto step = [&](int kt, auto ls, auto ss) {
+      if (PF > 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
+      if (kt + PF < KT) gload(kt + PF, decltype(ls)::value);
+      compute(kt & 1);
+      if (PF == 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % PF>;
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      // PF == 2: stage kt -> slot 0 (loaded into for kt + 2), stored from slot 1;
+      // PF == 1: single slot
+      step(kt, I0{}, I1{});
+      step(kt + 1, I1{}, I0{});
+    }
+    if (kt < KT) step(kt, I0{}, I1{});
   }
 
-  // ---- stage the fp32 tile in LDS as Cs[m][n] (acc[j][i] holds rows n, column m)
+  // ---------------------------------------------------------------- epilogues
+  // The fp32 tile is staged in LDS (the pipeline buffers are free after the last
+  // barrier): Cs[m][n] for row-wise epilogues, Cs[n][m] for the V columns of QKV.
+  // acc[j][i] = D[n][m]: lane holds row m, columns n..n+3.
+  static_assert(G::BM == 128 && G::BN == 128 && G::NT == 256, "epilogue assumes 128x128, 256 threads");
   float* Cs = reinterpret_cast<float*>(smem);
+  const bool vtile = EPI == kEpiQKV && n0 >= ep.vcol0;  // uniform per workgroup
+  if (vtile) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 64 + i * 16 + l16, n = wn * 64 + j * 16 + 4 * g;
-      *reinterpret_cast<f32x4*>(Cs + m * CS + n) = acc[j][i];
-    }
+      for (int i = 0; i < TM; ++i) {
+        const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Cs[(n + v) * kCS + m] = acc[j][i][v];
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
+        *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
+      }
+  }
   __syncthreads();
 
   const T* bias = static_cast<const T*>(ep.bias);
-  if (EPI == kEpiQKV && n0 >= ep.vcol0) {
-    // V columns: write V^T per head, [b][h][d][token]; lanes run along tokens so
-    // each store instruction covers consecutive tokens of one (head, d) row.
+  if (vtile) {
+    // V^T [b][h][d][token]: a wave writes 64 consecutive tokens of one channel per store
     T* vt = static_cast<T*>(ep.vt);
-    const int m = tid & 127, half = tid >> 7;
-    const int gm = m0 + m;
-    if (gm < M) {
-      const int bb = gm / ep.L, tk = gm - bb * ep.L;
+    const int mm = tid & 127, half = tid >> 7;
+    const int m = m0 + mm;
+    if (m < M) {
+      const int bb = m / ep.L, tk = m - bb * ep.L;
+      T* vrow = vt + (size_t)bb * ep.heads * 64 * ep.Lp + tk;
+#pragma unroll 4
       for (int jj = 0; jj < 64; ++jj) {
-        const int n = half * 64 + jj, gn = n0 + n;
-        if (gn < N) {
-          const int vc = gn - ep.vcol0, h = vc >> 6, d = vc & 63;
-          const float v = Cs[m * CS + n] + to_f32(bias[gn]);
-          vt[((size_t)(bb * ep.heads + h) * 64 + d) * ep.Lp + tk] = from_f32<T>(v);
-        }
+        const int nn = half * 64 + jj, n = n0 + nn;
+        if (n < N)
+          vrow[(size_t)(n - ep.vcol0) * ep.Lp] = from_f32<T>(Cs[nn * kCS + mm] + to_f32(bias[n]));
       }
     }
     return;
   }
 
-  // ---- row pass: 16 threads per row, 8 consecutive columns each
+  // row pass: 16 threads per row, 8 consecutive columns each
   const int er = tid >> 4, ec = (tid & 15) * 8;
-  const int gn = n0 + ec;
-  const bool col_ok = gn < N;
+  const int n = n0 + ec;
+  const bool col_ok = n < N;
   float b8[8];
-  if (col_ok) load8f(bias + gn, b8);
+  if (col_ok) load8f(bias + n, b8);
   T* out = static_cast<T*>(ep.out);
 #pragma unroll 1
-  for (int pass = 0; pass < BM / 16; ++pass) {
-    const int m = pass * 16 + er, gm = m0 + m;
-    const bool ok = col_ok && gm < M;
+  for (int pass = 0; pass < G::BM / 16; ++pass) {
+    const int mm = pass * 16 + er, m = m0 + mm;
+    const bool ok = col_ok && m < M;
     float v[8];
     {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(Cs + m * CS + ec);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(Cs + m * CS + ec + 4);
-      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(Cs + mm * kCS + ec);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(Cs + mm * kCS + ec + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi[e]; }
     }
     if (EPI == kEpiFc2) {
       float ss = 0.f;
       if (ok) {
         float xv[8], pv[8];
-        load8f(static_cast<const T*>(ep.x) + (size_t)gm * N + gn, xv);
-        load8f(static_cast<const T*>(ep.p) + (size_t)gm * N + gn, pv);
+        load8f(static_cast<const T*>(ep.x) + (size_t)m * N + n, xv);
+        load8f(static_cast<const T*>(ep.p) + (size_t)m * N + n, pv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float y = v[e] + b8[e];        // MLP(LN(x'))
-          const float xp = xv[e] + pv[e];      // x' (Eq. 5), fp32
+          const float y = v[e] + b8[e];   // MLP(LN(x'))
+          const float xp = xv[e] + pv[e]; // x' (Eq. 5), re-formed in fp32
           const float d = y - xp;
           ss += d * d;
-          v[e] = xp + y;                       // x_hat (Eq. 6)
+          v[e] = xp + y;                  // x_hat (Eq. 6)
         }
-        store8f(out + (size_t)gm * ep.ldo + gn, v);
+        store8f(out + (size_t)m * ep.ldo + n, v);
       }
       if (ep.part) {
-        ss = sum16(ss);
-        if ((tid & 15) == 0 && gm < M) ep.part[(size_t)gm * ep.nparts + nt] = ss;
+        // 8 lanes cover one 64-column wave slice of the row: one partial per slice
+        ss += __shfl_xor(ss, 4, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 1, 64);
+        if ((tid & 7) == 0 && m < M) ep.part[(size_t)m * ep.nparts + nt * 2 + ((tid >> 3) & 1)] = ss;
       }
     } else if (ok) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         v[e] += b8[e];
-        if (EPI == kEpiGelu) v[e] = gelu_erf(v[e]);
+        if (EPI == kEpiGelu) v[e] = gelu_t<T>(v[e]);
       }
-      store8f(out + (size_t)gm * ep.ldo + gn, v);
+      store8f(out + (size_t)m * ep.ldo + n, v);
     }
   }
 }
 
-template <typename T>
-hipError_t launch_t(GemmEpilogue epi, const void* A, const void* W, int M, int N, int K,
-                    const GemmEpiArgs& ep, hipStream_t st) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+template <typename T, class G>
+hipError_t launch_cfg(GemmEpilogue epi, const void* A, const void* W, int M, int N, int K,
+                      const GemmEpiArgs& ep, hipStream_t st) {
+  const int tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
   const T* a = static_cast<const T*>(A);
   const T* w = static_cast<const T*>(W);
   switch (epi) {
-    case kEpiQKV: gemm_nt_kernel<T, kEpiQKV><<<tiles, 256, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiBias: gemm_nt_kernel<T, kEpiBias><<<tiles, 256, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiGelu: gemm_nt_kernel<T, kEpiGelu><<<tiles, 256, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiFc2: gemm_nt_kernel<T, kEpiFc2><<<tiles, 256, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiQKV: gemm_kernel<T, kEpiQKV, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiBias: gemm_kernel<T, kEpiBias, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiGelu: gemm_kernel<T, kEpiGelu, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiFc2: gemm_kernel<T, kEpiFc2, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
   }
   return hipGetLastError();
 }
+
+// fc2 always runs with 2 waves of 64 columns across a 128-column tile, so the score
+// partial count per row is 2 * ceil(C / 128) (see score_parts()).
+template <typename T> using TileMain = Tile<T, 2, 2, 4, 4, 1>;
 
 }  // namespace
 
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
                        int K, const GemmEpiArgs& ep, hipStream_t stream) {
-  return dt == kBF16 ? launch_t<bf16>(epi, A, W, M, N, K, ep, stream)
-                     : launch_t<float>(epi, A, W, M, N, K, ep, stream);
+  if (dt == kBF16) return launch_cfg<bf16, TileMain<bf16>>(epi, A, W, M, N, K, ep, stream);
+  return launch_cfg<float, TileMain<float>>(epi, A, W, M, N, K, ep, stream);
 }
 
 }  // namespace rs

@@ -12,8 +12,9 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // Row tile of every GEMM: 128 activation rows x 128 output columns.
 constexpr int kGemmTile = 128;
-// Score partials per token written by the fc2 epilogue: one per 128-column tile.
-inline int score_parts(int C) { return (C + kGemmTile - 1) / kGemmTile; }
+// Score partials per token written by the fc2 epilogue: one per 64-column wave slice
+// of each 128-column tile.
+inline int score_parts(int C) { return 2 * ((C + kGemmTile - 1) / kGemmTile); }
 // Padded key length of the transposed V buffer (whole 64-key tiles).
 inline int padded_len(int L) { return (L + 63) / 64 * 64; }
 
@@ -28,7 +29,7 @@ struct GemmEpiArgs {
   const void* bias = nullptr;  // [N]
   void* out = nullptr;         // row stride ldo
   int ldo = 0;
-  // kEpiQKV
+  // kEpiQKV: output columns >= vcol0 (= 2C, a multiple of the tile width) are V
   void* vt = nullptr;
   int vcol0 = 0, L = 1, Lp = 64, heads = 1;
   // kEpiFc2: x' = x + p is re-formed in fp32 from the block input and the attention branch
