@@ -59,6 +59,108 @@ def cpu_baseline(wl, x, blocks, budget_s=12.0):
                       f"{wl.depth}-block pruned encoder, fp64 NumPy, {t_total:.1f} s"}
 
 
+# device kernel symbol (mangled) -> kernel class of the library's timing interface
+def kernel_class(mangled: str):
+    import re
+    m = re.search(r"gemm_kernelI(DF16b|f)Li(\d)E", mangled)
+    if m:
+        return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score"}[m.group(2)]
+    for key, name in (("attention_kernel", "attention"), ("layernorm_kernel", "layernorm"),
+                      ("topk_kernel", "topk"), ("gather_kernel", "gather"), ("score_kernel", "score")):
+        if key in mangled:
+            return name
+    return None
+
+
+def copy_probe(rs, torch):
+    """A plain copy of known size through the library's gather kernel: 2 GiB of bf16 rows,
+    all kept (k = L), so the gather reads and writes exactly 2 GiB (+ 512 KiB of indices).
+    At 8x the 256 MB Infinity Cache, at most ~1/8 of the source can be cache-resident."""
+    B, L, C = 8, 16384, 8192
+    x = torch.randn(B, L, C, device="cuda").to(torch.bfloat16)
+    s = torch.ones(B, L, device="cuda", dtype=torch.float32)
+    for _ in range(3):
+        rs.topk_gather(s, x, L, False)
+    torch.cuda.synchronize()
+    return B * L * C * 2
+
+
+def summarize(dirs, workload):
+    """Per-kernel averages of the counters in rocprofv3 result databases; HBM traffic of each
+    kernel class from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by what the same
+    counters read for the 256 MiB copy probe (the gather dispatch with the largest grid)."""
+    import collections
+    import glob
+    import sqlite3
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    probe = collections.defaultdict(list)
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            cur = sqlite3.connect(path).cursor()
+            names = dict(cur.execute("select id, kernel_name from kernel_symbols"))
+            disp = {r[0]: (r[1], r[2] * r[3] * r[4]) for r in cur.execute(
+                "select dispatch_id, kernel_id, grid_x, grid_y, grid_z from kernels")}
+            maxgrid = max((g for (kid, g) in disp.values() if kernel_class(names.get(kid, "")) == "gather"),
+                          default=None)
+            for did, cname, cval in cur.execute(
+                    "select dispatch_id, counter_name, sum(counter_value) from pmc_events "
+                    "group by dispatch_id, counter_name"):
+                kid, grid = disp.get(did, (None, 0))
+                kc = kernel_class(names.get(kid, ""))
+                if kc is None:
+                    continue
+                if kc == "gather" and grid == maxgrid:
+                    probe[cname].append(cval)
+                else:
+                    vals[kc][cname].append(cval)
+    known = 8 * 16384 * 8192 * 2
+    out = {"workload": workload, "kernels": {}}
+    fac = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if probe.get(c):
+            fac[c] = known / (sum(probe[c]) / len(probe[c]) * 1024.0)
+    out["copy_probe"] = {"bytes_each_way": known,
+                         **{c: sum(v) / len(v) for c, v in probe.items()}, "scale": fac}
+    for kc, cs in vals.items():
+        row = {c: sum(v) / len(v) for c, v in cs.items()}
+        row["dispatches"] = max(len(v) for v in cs.values())
+        t = 0.0
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in row and c in fac:
+                row[c + "_bytes"] = row[c] * 1024.0 * fac[c]
+                t += row[c + "_bytes"]
+        if "FETCH_SIZE_bytes" in row and "WRITE_SIZE_bytes" in row:
+            row["traffic_bytes_per_launch"] = t
+        out["kernels"][kc] = row
+    out["kernel_sources_sha256"] = kernel_sources_sha256()
+    return out
+
+
+def kernel_sources_sha256():
+    import hashlib
+    src = os.path.join(ROOT, "vit_token_pruning_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<workload>.json, only if the
+    counters were taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    k = t.get("kernels", {}).get(kernel, {})
+    v = k.get("traffic_bytes_per_launch")
+    return None if v is None else float(v)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,8 +168,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="deit_s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 256 MiB copy through the gather kernel (counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 --pmc result directories and exit (no GPU use)")
     args = ap.parse_args()
+    if args.summarize:
+        print(json.dumps(summarize(args.summarize, args.workload), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path shards by sample with no communication; see the design notes)",
@@ -130,7 +238,8 @@ def main():
         achieved = kt.work / (kt.total_ms / 1e3) / 1e9
         unit = "GB/s"
     roof = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK[bound],
-            "unit": unit, "frac": round(achieved / PEAK[bound], 4), "traffic": None,
+            "unit": unit, "frac": round(achieved / PEAK[bound], 4),
+            "traffic": stored_traffic(wl.name, dominant),
             "launches_per_step": kt.launches // args.steps,
             "avg_launch_us": round(kt.total_ms * 1e3 / max(1, kt.launches), 3)}
 
@@ -157,6 +266,8 @@ def main():
         "roofline": roof,
         "kernel_ms_per_step": {k: round(v["ms"], 4) for k, v in per.items()},
     }
+    if args.copy_probe:
+        copy_probe(rs, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x_np, blocks_np)
     print(json.dumps(line), flush=True)
