@@ -13,8 +13,9 @@
 //    lane's own output registers, and the probabilities are already in the register
 //    layout the P V product wants as its B operand (no LDS round trip for P).
 //  - K tiles [64 keys][64 d] and V^T tiles [64 d][64 keys] are staged in LDS, double
-//    buffered; V^T comes pre-transposed from the QKV epilogue, so both products read
-//    K-contiguous fragments.
+//    buffered, each row padded by 16 bytes so the 16 rows of a fragment read fall on
+//    distinct banks; V^T comes pre-transposed from the QKV epilogue, so both products
+//    read K-contiguous fragments.
 //  - exp2 with log2(e)/sqrt(d) folded into one FMA per score; the hardware exp2 is used
 //    directly (results below 2^-126 flush to zero, which a softmax over at least one
 //    term equal to 1 cannot notice).
@@ -68,15 +69,19 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
                                                         T* __restrict__ out, int L, int H, int Lp,
                                                         float scale_log2) {
   constexpr int CB = Chunk<T>::bytes;  // 8 elements
-  constexpr int ROWB = 8 * CB;         // 64 elements
+  constexpr int ROWB = 8 * CB + 16;    // 64 elements + 16 bytes of padding
   constexpr int TB = 64 * ROWB;        // one 64 x 64 tile
   __shared__ __attribute__((aligned(16))) char smem[4 * TB];
 
   const int C = H * 64, ldqk = 2 * C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int q0 = blockIdx.x * 64 + wave * 16;
+  // launch index -> (query block, head, sample), query blocks fastest; each XCD gets a
+  // contiguous range so the query blocks of one head re-read its K/V from one L2
+  const int nq = (L + 63) >> 6;
+  const int t = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int qb = t % nq, h = (t / nq) % H, b = t / (nq * H);
+  const int q0 = qb * 64 + wave * 16;
   const size_t row0 = (size_t)b * L;
 
   // Q as the B operand: lane (g, l16) holds query q0+l16, d = 32ks + 8g .. +7
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = lr + 32 * i;
-      const int off = r * ROWB + ((lc ^ (r & 7)) * CB);
+      const int off = r * ROWB + lc * CB;
       store_frag(Ks + off, rk[i]);
       store_frag(Vs + off, rv[i]);
     }
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
       for (int ks = 0; ks < 2; ++ks) {
         const int c = ks * 4 + g;
         Frag8<T> kf;
-        load_frag(kf, Ks + r * ROWB + ((c ^ (r & 7)) * CB));
+        load_frag(kf, Ks + r * ROWB + c * CB);
         s[j] = mma16(s[j], kf, qf[ks]);
       }
     }
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
         const int ca = 4 * kc + (g >> 1), cb = ca + 2;
         const int half = (g & 1) * (CB / 2);
         Frag8<T> vf;
-        load_vt(vf, vrow + ((ca ^ (r & 7)) * CB) + half, vrow + ((cb ^ (r & 7)) * CB) + half);
+        load_vt(vf, vrow + ca * CB + half, vrow + cb * CB + half);
         o[d] = mma16(o[d], vf, pf[kc]);
       }
     }
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 hipError_t launch_attention(Dtype dt, const void* qk, const void* vt, void* out, int B, int L,
                             int H, int Lp, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-  const dim3 grid((L + 63) / 64, H, B);
+  const int grid = ((L + 63) / 64) * H * B;
   if (dt == kBF16)
     attention_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(qk),
                                                      static_cast<const bf16*>(vt),
