@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roofline"
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
-                "fc2_score": "mfma", "layernorm": "hbm", "topk": "hbm", "gather": "hbm",
+                "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm", "gather": "hbm",
                 "score": "hbm"}
 
 
@@ -65,7 +65,7 @@ def kernel_class(mangled: str):
     m = re.search(r"gemm_kernelI(DF16b|f)Li(\d)E", mangled)
     if m:
         return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score"}[m.group(2)]
-    for key, name in (("attention_kernel", "attention"), ("layernorm_kernel", "layernorm"),
+    for key, name in (("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
                       ("topk_kernel", "topk"), ("gather_kernel", "gather"), ("score_kernel", "score")):
         if key in mangled:
             return name

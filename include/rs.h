@@ -140,9 +140,12 @@ const char* rs_last_error(void);
  * launched on.  rs_timing_end() waits for those events and returns the summed kernel
  * time, the number of launches and the summed algorithmic work of those launches
  * (flop for the GEMM and attention kernels, bytes for the memory-bound ones).
+ * LayerNorm has no pass of its own: it is folded into the QKV and fc1 GEMMs, whose inputs'
+ * row statistics come from the producing epilogue; RS_KERNEL_LN_PREP times the remaining
+ * preparation (statistics of the encoder input, per-call weight folding).
  * One timing session at a time per process. */
 typedef enum {
-  RS_KERNEL_LAYERNORM = 0,
+  RS_KERNEL_LN_PREP = 0,      /* LayerNorm statistics and weight folding */
   RS_KERNEL_QKV = 1,
   RS_KERNEL_ATTENTION = 2,
   RS_KERNEL_PROJ = 3,

@@ -145,7 +145,10 @@ def test_workspace_query(N):
     d = _desc(N)
     a = lib.rs_workspace_bytes(ctypes.byref(d), 1, 256, 197)
     b = lib.rs_workspace_bytes(ctypes.byref(d), 12, 256, 197)
-    assert a == b and a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
+    # activations for one block plus the LayerNorm-folded weights of every block
+    fold = 3 * 384 * 384 * 2
+    assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
+    assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
 
 
 def test_timing_session_without_launches(N):

@@ -13,7 +13,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rs.h")
 
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
-KERNELS = ("layernorm", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score")
+KERNELS = ("ln_prep", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score")
 
 # field order of rs_block_weights
 BLOCK_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj",

@@ -141,33 +141,61 @@ rs_status check_schedule(int depth, int L, const int* prune, const double* ratio
 
 // ------------------------------------------------------------------ workspace
 struct BlockWs {
-  void *xn, *qk, *vt, *o, *p, *h, *xhat;
-  float* part;
+  void *qk, *vt, *o, *p, *xp, *h, *xhat;
+  float* part;    // score partials of x_hat rows
+  float* st_x;    // slice partials of the block input rows (LayerNorm 1)
+  float* st_xp;   // slice partials of x' rows (LayerNorm 2)
+  float* st_xhat; // slice partials of x_hat rows (next block's LayerNorm 1)
 };
+struct FoldWs {   // LayerNorm folding of one block: W_qkv diag(gamma1); c, d of QKV and fc1
+  void* wq;
+  float *cq, *dq, *c1, *d1;
+};
+
+size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    ptrs[i] = base ? base + off : nullptr;
+    off += up256(sizes[i]);
+  }
+  return off;
+}
 
 // Carves the per-block buffers for (B, L) from `base` (or only sizes them if null).
 size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws) {
   const size_t e = esize(d.dtype), M = (size_t)B * L, C = d.C;
-  const size_t sizes[8] = {
-      up256(M * C * e),                                  // xn: LN output
-      up256(M * 2 * C * e),                              // qk: Q | K
-      up256((size_t)B * d.heads * 64 * rs::padded_len(L) * e),  // vt: V^T per head
-      up256(M * C * e),                                  // o: attention output
-      up256(M * C * e),                                  // p: attention branch (proj out)
-      up256(M * (size_t)d.hidden * e),                   // h: GELU(fc1)
-      up256(M * C * e),                                  // xhat: block output
-      up256(M * (size_t)rs::score_parts(d.C) * 4),       // part: score partials
+  const size_t st = M * rs::stat_stride(d.C) * 8;
+  const size_t sizes[11] = {
+      M * 2 * C * e,                                     // qk: Q | K
+      (size_t)B * d.heads * 64 * rs::padded_len(L) * e,  // vt: V^T per head
+      M * C * e,                                         // o: attention output
+      M * C * e,                                         // p: attention branch (proj out)
+      M * C * e,                                         // xp: x' * gamma2 (fc1 input)
+      M * (size_t)d.hidden * e,                          // h: GELU(fc1)
+      M * C * e,                                         // xhat: block output
+      M * (size_t)rs::score_parts(d.C) * 4,              // part: score partials
+      st, st, st,                                        // slice partials
   };
-  size_t off = 0;
-  void* ptrs[8];
-  for (int i = 0; i < 8; ++i) {
-    ptrs[i] = base ? base + off : nullptr;
-    off += sizes[i];
-  }
+  void* p[11];
+  const size_t off = carve_seq(base, sizes, 11, p);
   if (ws) {
-    ws->xn = ptrs[0]; ws->qk = ptrs[1]; ws->vt = ptrs[2]; ws->o = ptrs[3];
-    ws->p = ptrs[4]; ws->h = ptrs[5]; ws->xhat = ptrs[6];
-    ws->part = static_cast<float*>(ptrs[7]);
+    ws->qk = p[0]; ws->vt = p[1]; ws->o = p[2]; ws->p = p[3]; ws->xp = p[4]; ws->h = p[5];
+    ws->xhat = p[6]; ws->part = static_cast<float*>(p[7]);
+    ws->st_x = static_cast<float*>(p[8]); ws->st_xp = static_cast<float*>(p[9]);
+    ws->st_xhat = static_cast<float*>(p[10]);
+  }
+  return off;
+}
+
+size_t carve_fold(const rs_model_desc& d, char* base, FoldWs* fw) {
+  const size_t e = esize(d.dtype), C = d.C, Hd = d.hidden;
+  const size_t sizes[5] = {3 * C * C * e, 3 * C * 4, 3 * C * 4, Hd * 4, Hd * 4};
+  void* p[5];
+  const size_t off = carve_seq(base, sizes, 5, p);
+  if (fw) {
+    fw->wq = p[0];
+    fw->cq = static_cast<float*>(p[1]); fw->dq = static_cast<float*>(p[2]);
+    fw->c1 = static_cast<float*>(p[3]); fw->d1 = static_cast<float*>(p[4]);
   }
   return off;
 }
@@ -177,19 +205,30 @@ struct EncWs {
   void* act;      // [B][L][C] running activations
   int32_t* kept;  // [B][L]
   int32_t* ids[2];
+  char* fold;     // depth x carve_fold
 };
 
-size_t carve_encoder(const rs_model_desc& d, int B, int L, char* base, EncWs* ws) {
+// Workspace of rs_block_forward (nfold = 1) and rs_encoder_forward (nfold = depth).
+size_t carve_encoder(const rs_model_desc& d, int nfold, int B, int L, char* base, EncWs* ws) {
   size_t off = carve_block(d, B, L, base, ws ? &ws->blk : nullptr);
-  const size_t act = up256((size_t)B * L * d.C * esize(d.dtype));
-  const size_t idb = up256((size_t)B * L * 4);
+  const size_t sizes[4] = {(size_t)B * L * d.C * esize(d.dtype), (size_t)B * L * 4,
+                           (size_t)B * L * 4, (size_t)B * L * 4};
+  void* p[4];
+  off += carve_seq(base ? base + off : nullptr, sizes, 4, p);
   if (ws) {
-    ws->act = base + off;
-    ws->kept = reinterpret_cast<int32_t*>(base + off + act);
-    ws->ids[0] = reinterpret_cast<int32_t*>(base + off + act + idb);
-    ws->ids[1] = reinterpret_cast<int32_t*>(base + off + act + 2 * idb);
+    ws->act = p[0];
+    ws->kept = static_cast<int32_t*>(p[1]);
+    ws->ids[0] = static_cast<int32_t*>(p[2]);
+    ws->ids[1] = static_cast<int32_t*>(p[3]);
+    ws->fold = base + off;
   }
-  return off + act + 3 * idb;
+  return off + (size_t)nfold * carve_fold(d, nullptr, nullptr);
+}
+
+FoldWs fold_of(const rs_model_desc& d, const EncWs& ws, int b) {
+  FoldWs fw;
+  carve_fold(d, ws.fold + (size_t)b * carve_fold(d, nullptr, nullptr), &fw);
+  return fw;
 }
 
 // ------------------------------------------------------------------ launch sequence
@@ -199,26 +238,55 @@ size_t carve_encoder(const rs_model_desc& d, int B, int L, char* base, EncWs* ws
     if (e_ != hipSuccess) return fail(RS_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
-// One block: Eq. (5) then Eq. (6); the fc2 epilogue writes x_hat to `out` and, if
-// `part` is not null, the per-token partial sums of the squared MLP-sublayer shift.
-// `out` may alias `x` (the fc2 epilogue reads each element of x before it writes it,
-// and nothing reads x after that).
-rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const void* x, int B, int L,
-                    void* out, float* part, const BlockWs& ws, hipStream_t st) {
-  const rs::Dtype dt = d.dtype == RS_BF16 ? rs::kBF16 : rs::kF32;
-  const int M = B * L, C = d.C, Hd = d.hidden;
-  const double e = (double)esize(d.dtype);
-  const double Md = M, Cd = C;
+rs::Dtype dtype_of(const rs_model_desc& d) { return d.dtype == RS_BF16 ? rs::kBF16 : rs::kF32; }
 
-  RS_HIP(timed(RS_KERNEL_LAYERNORM, Md * Cd * e * 2, st, [&] {
-    return rs::launch_layernorm(dt, x, nullptr, w.ln1_g, w.ln1_b, d.ln_eps, ws.xn, M, C, st);
+// LayerNorm folding of blocks [b0, b0 + n): W_qkv diag(gamma1) with its c, d, and c, d of
+// fc1 against gamma2/beta2; up to four blocks (eight weights) per launch.
+rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const EncWs& ws, int b0,
+                   int n, hipStream_t st) {
+  for (int b = b0; b < b0 + n; b += rs::kMaxFoldJobs / 2) {
+    rs::FoldJob jobs[rs::kMaxFoldJobs];
+    int nj = 0;
+    double bytes = 0.0;
+    for (int i = b; i < b0 + n && i < b + rs::kMaxFoldJobs / 2; ++i) {
+      const rs_block_weights& w = blocks[i - b0];
+      const FoldWs fw = fold_of(d, ws, i - b0);
+      jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, fw.wq, fw.cq, fw.dq, 3 * d.C};
+      jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
+      bytes += (2.0 * 3.0 * d.C + d.hidden) * d.C * esize(d.dtype);
+    }
+    RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
+      return rs::launch_fold(dtype_of(d), jobs, nj, d.C, st);
+    }));
+  }
+  return RS_OK;
+}
+
+rs_status run_row_stats(const rs_model_desc& d, const void* x, float* stats, int M, hipStream_t st) {
+  RS_HIP(timed(RS_KERNEL_LN_PREP, (double)M * d.C * esize(d.dtype), st, [&] {
+    return rs::launch_row_stats(dtype_of(d), x, stats, M, d.C, st);
   }));
+  return RS_OK;
+}
+
+// One block: Eq. (5) then Eq. (6), LayerNorms folded.  st_x holds the slice partials of
+// the rows of x.  The fc2 epilogue writes x_hat to `out`, the score partials to `part`
+// (nullable) and the slice partials of x_hat to `st_out` (nullable; may alias st_x, which
+// nothing reads after the QKV epilogue).  `out` may alias `x` (the fc2 epilogue reads each
+// element of x before it writes it, and nothing reads x after that).
+rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const FoldWs& fw,
+                    const void* x, const float* st_x, int B, int L, void* out, float* part,
+                    float* st_out, const BlockWs& ws, hipStream_t st) {
+  const rs::Dtype dt = dtype_of(d);
+  const int M = B * L, C = d.C, Hd = d.hidden;
+  const double Md = M, Cd = C;
   {
     rs::GemmEpiArgs ep;
-    ep.bias = w.b_qkv; ep.out = ws.qk; ep.ldo = 2 * C;
+    ep.out = ws.qk; ep.ldo = 2 * C;
     ep.vt = ws.vt; ep.vcol0 = 2 * C; ep.L = L; ep.Lp = rs::padded_len(L); ep.heads = d.heads;
+    ep.stats_in = st_x; ep.fold_c = fw.cq; ep.fold_d = fw.dq; ep.eps = d.ln_eps; ep.C = C;
     RS_HIP(timed(RS_KERNEL_QKV, 2.0 * Md * 3 * Cd * Cd, st, [&] {
-      return rs::launch_gemm(dt, rs::kEpiQKV, ws.xn, w.w_qkv, M, 3 * C, C, ep, st);
+      return rs::launch_gemm(dt, rs::kEpiQKV, x, fw.wq, M, 3 * C, C, ep, st);
     }));
   }
   RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
@@ -227,24 +295,24 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const voi
   {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
+    ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
-      return rs::launch_gemm(dt, rs::kEpiBias, ws.o, w.w_proj, M, C, C, ep, st);
+      return rs::launch_gemm(dt, rs::kEpiProj, ws.o, w.w_proj, M, C, C, ep, st);
     }));
   }
-  RS_HIP(timed(RS_KERNEL_LAYERNORM, Md * Cd * e * 3, st, [&] {
-    return rs::launch_layernorm(dt, x, ws.p, w.ln2_g, w.ln2_b, d.ln_eps, ws.xn, M, C, st);
-  }));
   {
     rs::GemmEpiArgs ep;
-    ep.bias = w.b_fc1; ep.out = ws.h; ep.ldo = Hd;
+    ep.out = ws.h; ep.ldo = Hd;
+    ep.stats_in = ws.st_xp; ep.fold_c = fw.c1; ep.fold_d = fw.d1; ep.eps = d.ln_eps; ep.C = C;
     RS_HIP(timed(RS_KERNEL_FC1, 2.0 * Md * Cd * Hd, st, [&] {
-      return rs::launch_gemm(dt, rs::kEpiGelu, ws.xn, w.w_fc1, M, Hd, C, ep, st);
+      return rs::launch_gemm(dt, rs::kEpiGelu, ws.xp, w.w_fc1, M, Hd, C, ep, st);
     }));
   }
   {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
     ep.x = x; ep.p = ws.p; ep.part = part; ep.nparts = rs::score_parts(C);
+    ep.stats_out = st_out; ep.C = C;
     RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
     }));
@@ -282,8 +350,7 @@ size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L) {
     g_err = saved;
     return 0;
   }
-  // one size serves both entry points: the encoder's carve contains the block's
-  return carve_encoder(*desc, B, L, nullptr, nullptr);
+  return carve_encoder(*desc, depth, B, L, nullptr, nullptr);
 }
 
 rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers, const double* keep_ratios,
@@ -307,17 +374,21 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
   if ((s = check_ptr(kept_idx, "kept_idx")) != RS_OK) return s;
   if ((s = check_ptr(y_kept, "y_kept")) != RS_OK) return s;
   if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
-  const size_t need = carve_block(*desc, B, L, nullptr, nullptr);
+  const size_t need = carve_encoder(*desc, 1, B, L, nullptr, nullptr);
   if (ws_bytes < need)
     return fail(RS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
 
-  BlockWs ws;
-  carve_block(*desc, B, L, static_cast<char*>(workspace), &ws);
-  void* xhat = y ? y : ws.xhat;
-  if ((s = run_block(*desc, *w, x, B, L, xhat, ws.part, ws, stream)) != RS_OK) return s;
-  return run_select(B, L, keep_k, desc->has_cls, nullptr, ws.part, rs::score_parts(desc->C), scores,
-                    kept_idx, nullptr, nullptr, xhat, y_kept, (size_t)desc->C * esize(desc->dtype),
-                    stream);
+  EncWs ws;
+  carve_encoder(*desc, 1, B, L, static_cast<char*>(workspace), &ws);
+  void* xhat = y ? y : ws.blk.xhat;
+  if ((s = run_fold(*desc, w, ws, 0, 1, stream)) != RS_OK) return s;
+  if ((s = run_row_stats(*desc, x, ws.blk.st_x, B * L, stream)) != RS_OK) return s;
+  if ((s = run_block(*desc, *w, fold_of(*desc, ws, 0), x, ws.blk.st_x, B, L, xhat, ws.blk.part,
+                     nullptr, ws.blk, stream)) != RS_OK)
+    return s;
+  return run_select(B, L, keep_k, desc->has_cls, nullptr, ws.blk.part, rs::score_parts(desc->C),
+                    scores, kept_idx, nullptr, nullptr, xhat, y_kept,
+                    (size_t)desc->C * esize(desc->dtype), stream);
 }
 
 rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype, float* scores,
@@ -374,23 +445,29 @@ rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* 
   if ((s = check_ptr(out, "out")) != RS_OK) return s;
   if ((s = check_ptr(out_idx, "out_idx", 4)) != RS_OK) return s;
   if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
-  const size_t need = carve_encoder(*desc, B, L, nullptr, nullptr);
+  const size_t need = carve_encoder(*desc, depth, B, L, nullptr, nullptr);
   if (ws_bytes < need)
     return fail(RS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
 
   EncWs ws;
-  carve_encoder(*desc, B, L, static_cast<char*>(workspace), &ws);
+  carve_encoder(*desc, depth, B, L, static_cast<char*>(workspace), &ws);
   const size_t row_bytes = (size_t)desc->C * esize(desc->dtype);
+  const size_t stat_bytes = (size_t)rs::stat_stride(desc->C) * 8;
   const int P = rs::score_parts(desc->C);
-  const void* cur = x;  // block input
+  if ((s = run_fold(*desc, blocks, ws, 0, depth, stream)) != RS_OK) return s;
+  if ((s = run_row_stats(*desc, x, ws.blk.st_x, B * L, stream)) != RS_OK) return s;
+  const void* cur = x;  // block input; its slice partials are always in ws.blk.st_x
   int curL = L, pi = 0;
   const int32_t* ids = nullptr;  // original ids of the current rows (null = identity)
   for (int b = 0; b < depth; ++b) {
     const bool prune = pi < n_prune && prune_layers[pi] == b;
     const bool last = b == depth - 1;
+    const FoldWs fw = fold_of(*desc, ws, b);
     if (!prune) {
       void* dst = last ? out : ws.act;
-      if ((s = run_block(*desc, blocks[b], cur, B, curL, dst, nullptr, ws.blk, stream)) != RS_OK) return s;
+      if ((s = run_block(*desc, blocks[b], fw, cur, ws.blk.st_x, B, curL, dst, nullptr,
+                         last ? nullptr : ws.blk.st_x, ws.blk, stream)) != RS_OK)
+        return s;
       cur = dst;
       continue;
     }
@@ -398,11 +475,19 @@ rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* 
     const bool last_prune = pi == n_prune - 1;
     int32_t* ids_out = last_prune ? out_idx : ws.ids[pi & 1];
     void* dst = last ? out : ws.act;
-    if ((s = run_block(*desc, blocks[b], cur, B, curL, ws.blk.xhat, ws.blk.part, ws.blk, stream)) != RS_OK)
+    if ((s = run_block(*desc, blocks[b], fw, cur, ws.blk.st_x, B, curL, ws.blk.xhat, ws.blk.part,
+                       last ? nullptr : ws.blk.st_xhat, ws.blk, stream)) != RS_OK)
       return s;
     if ((s = run_select(B, curL, k, desc->has_cls, nullptr, ws.blk.part, P, nullptr, ws.kept, ids,
                         ids_out, ws.blk.xhat, dst, row_bytes, stream)) != RS_OK)
       return s;
+    if (!last) {
+      // the kept rows' LayerNorm statistics follow them
+      RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)stat_bytes, stream, [&] {
+        return rs::launch_gather(ws.blk.st_xhat, ws.kept, ws.blk.st_x, B, curL, k, (int)stat_bytes,
+                                 stream);
+      }));
+    }
     cur = dst;
     ids = ids_out;
     curL = k;

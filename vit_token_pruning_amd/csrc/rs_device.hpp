@@ -86,11 +86,31 @@ __device__ __forceinline__ void store8f(float* p, const float* f) {
   ((f32x4*)p)[0] = f32x4{f[0], f[1], f[2], f[3]};
   ((f32x4*)p)[1] = f32x4{f[4], f[5], f[6], f[7]};
 }
+__device__ __forceinline__ void frag_to_f32(const Frag8<bf16>& f, float* o) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o[2 * e] = bf16_lo(f.v[e]); o[2 * e + 1] = bf16_hi(f.v[e]); }
+}
+__device__ __forceinline__ void frag_to_f32(const Frag8<float>& f, float* o) {
+  const f32x4 a = __builtin_bit_cast(f32x4, f.v[0]);
+  const f32x4 b = __builtin_bit_cast(f32x4, f.v[1]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = a[e];
+    o[4 + e] = b[e];
+  }
+}
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// the value a float takes once stored as T
+template <typename T> __device__ __forceinline__ float round_t(float v) { return to_f32(from_f32<T>(v)); }
+
+
+// Merge of equal-count slice partials (slice mean m_s, slice sum of squared deviations
+// M2_s, 64 values each) into the row's mean and biased variance:
+//   mean = avg(m_s),  M2 = sum(M2_s) + 64 * sum((m_s - mean)^2),  var = M2 / (64 * P).
 
 // ---- wavefront reductions (64 lanes) -------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
@@ -98,10 +118,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Lane exchanges inside a row of 16 lanes with DPP (plain VALU ops, no LDS routing):
+// quad_perm [1,0,3,2] / [2,3,0,1], row_half_mirror (lane i <-> 7-i within 8),
+// row_mirror (lane i <-> 15-i within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 8 consecutive lanes that share (lane / 8)
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: every lane holds its quad's sum
+  v += dpp<0x141>(v);  // row_half_mirror: adds the other quad of the 8
+  return v;
+}
 // sum over the 16 consecutive lanes that share (lane / 16)
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = sum8(v);
+  v += dpp<0x140>(v);  // row_mirror: adds the other 8 of the 16
   return v;
 }
 

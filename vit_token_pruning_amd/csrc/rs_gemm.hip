@@ -1,7 +1,17 @@
 // Tile GEMM Y = A W^T on the gfx950 matrix cores with the block's fused epilogues:
-// QKV (bias, per-head transposed V), attention projection (bias), fc1 (bias + GELU)
-// and fc2 (bias, residual re-formed in fp32, and the per-token partial sums of squares
-// of the MLP-sublayer representation shift).
+// QKV (LayerNorm 1 folded in, per-head transposed V), attention projection (bias,
+// x' = x + p, LayerNorm 2 statistics), fc1 (LayerNorm 2 folded in, GELU) and fc2 (bias,
+// residual re-formed in fp32, the per-token partial sums of squares of the MLP-sublayer
+// representation shift, and the next block's LayerNorm 1 statistics).
+//
+// LayerNorm (Sec. 3.3, Eqs. (5) and (6)) is applied without a pass of its own.  With row
+// mean mu and 1/std rstd, LN(z) W^T + b = rstd ((z * gamma) W^T - mu c) + d, c = W gamma,
+// d = W beta + b.  LayerNorm 1: the GEMM consumes the raw block input z = x against
+// W' = W diag(gamma) (c = W' 1), prepared per call with c and d (rs_rowops.hip,
+// fold_kernel).  LayerNorm 2: the projection epilogue, which forms x' in fp32, stores
+// x' * gamma for fc1 (one rounding, as a LayerNorm output would have), and fc1 uses its
+// own weights.  Row statistics arrive as per-64-column slice partials from the kernel
+// that produced the rows.
 //
 // The score is Eq. (4) of "Representation Shift: Unifying Token Compression with
 // FlashAttention" (arXiv HTML), Sec. 3.2, for the MLP sublayer of Sec. 3.3 (case ii)
@@ -68,7 +78,8 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
                                                      int K, GemmEpiArgs ep) {
   constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
   constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
-  constexpr int SMEM = 2 * STAGE > G::BM * kCS * 4 ? 2 * STAGE : G::BM * kCS * 4;
+  // pipeline stages, or the staged fp32 tile plus one float2 per tile row
+  constexpr int SMEM = 2 * STAGE > G::BM * kCS * 4 + G::BM * 8 ? 2 * STAGE : G::BM * kCS * 4 + G::BM * 8;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -173,6 +184,38 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   }
 
   // ---------------------------------------------------------------- epilogues
+  // Epilogue inputs from global memory (row statistics, x, p) for all of this thread's
+  // rows are requested here, before the tile is staged, so their latency overlaps the
+  // staging instead of being paid once per row pass.
+  constexpr int NPASS = G::BM / 16;
+  constexpr bool kFoldE = EPI == kEpiQKV || EPI == kEpiGelu;
+  constexpr bool kResid = EPI == kEpiProj || EPI == kEpiFc2;
+  const int e_er = tid >> 4, e_sub = tid & 15, e_n = n0 + e_sub * 8;
+  const int e_nsl = stat_slices(ep.C), e_stride = stat_stride(ep.C);
+  const bool e_vt = EPI == kEpiQKV && n0 >= ep.vcol0;
+  // kFoldE: thread t < 128 fetches all slice partials of tile row t (at most 16)
+  float2 rpart[16];
+  if (kFoldE && tid < G::BM) {
+    const int m = m0 + tid;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      rpart[q] = make_float2(0.f, 0.f);
+      if (q < e_nsl && m < M)
+        rpart[q] = *reinterpret_cast<const float2*>(ep.stats_in + ((size_t)m * e_stride + q) * 2);
+    }
+  }
+  Frag8<T> px[NPASS], pp[NPASS];           // kResid: x (and p) of each row
+  if (!e_vt) {
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int m = m0 + pass * 16 + e_er;
+      if (kResid && m < M && e_n < N) {
+        load_frag(px[pass], static_cast<const T*>(ep.x) + (size_t)m * N + e_n);
+        if (EPI == kEpiFc2) load_frag(pp[pass], static_cast<const T*>(ep.p) + (size_t)m * N + e_n);
+      }
+    }
+  }
+
   // The fp32 tile is staged in LDS (the pipeline buffers are free after the last
   // barrier): Cs[m][n] for row-wise epilogues, Cs[n][m] for the V columns of QKV.
   // acc[j][i] = D[n][m]: lane holds row m, columns n..n+3.
@@ -197,38 +240,71 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
         *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
       }
   }
+  // folded LayerNorm: each tile row's (mean * rstd, rstd), merged once from its slice
+  // partials (equal-count merge) and shared through LDS
+  float2* Rs = reinterpret_cast<float2*>(smem + G::BM * kCS * 4);
+  if (kFoldE && tid < G::BM) {
+    float mean = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mean += rpart[q].x;  // absent slices hold 0
+    mean /= (float)e_nsl;
+    float m2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (q < e_nsl) {
+        const float dm = rpart[q].x - mean;
+        m2 += rpart[q].y + 64.f * dm * dm;
+      }
+    const float rstd = 1.0f / sqrtf(m2 / (float)ep.C + ep.eps);
+    Rs[tid] = make_float2(mean * rstd, rstd);
+  }
   __syncthreads();
 
   const T* bias = static_cast<const T*>(ep.bias);
+  constexpr bool kFold = kFoldE;  // LayerNorm folded into A
+  const int nsl = e_nsl;
   if (vtile) {
     // V^T [b][h][d][token]: a wave writes 64 consecutive tokens of one channel per store
     T* vt = static_cast<T*>(ep.vt);
     const int mm = tid & 127, half = tid >> 7;
     const int m = m0 + mm;
     if (m < M) {
+      const float mr = Rs[mm].x, rstd = Rs[mm].y;
       const int bb = m / ep.L, tk = m - bb * ep.L;
       T* vrow = vt + (size_t)bb * ep.heads * 64 * ep.Lp + tk;
 #pragma unroll 4
       for (int jj = 0; jj < 64; ++jj) {
         const int nn = half * 64 + jj, n = n0 + nn;
-        if (n < N)
-          vrow[(size_t)(n - ep.vcol0) * ep.Lp] = from_f32<T>(Cs[nn * kCS + mm] + to_f32(bias[n]));
+        if (n < N) {
+          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, ep.fold_c[n], ep.fold_d[n]));
+          vrow[(size_t)(n - ep.vcol0) * ep.Lp] = from_f32<T>(v);
+        }
       }
     }
     return;
   }
 
-  // row pass: 16 threads per row, 8 consecutive columns each
-  const int er = tid >> 4, ec = (tid & 15) * 8;
+  // row pass: 16 threads per row, 8 consecutive columns each; lanes 0-7 / 8-15 of a row
+  // cover its two 64-column slices of this tile
+  const int er = tid >> 4, sub = tid & 15, ec = sub * 8;
   const int n = n0 + ec;
   const bool col_ok = n < N;
-  float b8[8];
-  if (col_ok) load8f(bias + n, b8);
+  const int slice = nt * 2 + (sub >> 3);          // 64-column slice of the row
+  float b8[8], c8[8], d8[8];
+  if (kFold) {
+    if (col_ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
+    }
+  } else if (col_ok) {
+    load8f(bias + n, b8);
+  }
   T* out = static_cast<T*>(ep.out);
-#pragma unroll 1
-  for (int pass = 0; pass < G::BM / 16; ++pass) {
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
     const int mm = pass * 16 + er, m = m0 + mm;
-    const bool ok = col_ok && m < M;
+    const bool row_ok = m < M;
+    const bool ok = col_ok && row_ok;
     float v[8];
     {
       const f32x4 lo = *reinterpret_cast<const f32x4*>(Cs + mm * kCS + ec);
@@ -236,36 +312,71 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi[e]; }
     }
-    if (EPI == kEpiFc2) {
-      float ss = 0.f;
+    if (kFold) {
+      const float mr = Rs[mm].x, rstd = Rs[mm].y;
       if (ok) {
-        float xv[8], pv[8];
-        load8f(static_cast<const T*>(ep.x) + (size_t)m * N + n, xv);
-        load8f(static_cast<const T*>(ep.p) + (size_t)m * N + n, pv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] = fmaf(rstd, v[e], fmaf(-mr, c8[e], d8[e]));   // rstd (acc - mean c) + d
+          if (EPI == kEpiGelu) v[e] = gelu_t<T>(v[e]);
+        }
+        store8f(out + (size_t)m * ep.ldo + n, v);
+      }
+      continue;
+    }
+    // kEpiProj / kEpiFc2: the output row in fp32 plus its slice partials
+    float sdev = 0.f;      // fc2: squared representation shift over this thread's columns
+    float w[8];            // stored values whose slice partials are emitted
+    if (ok) {
+      float xv[8], pv[8];
+      frag_to_f32(px[pass], xv);
+      if (EPI == kEpiProj) {
+        float g8[8], u[8];
+        load8f(static_cast<const T*>(ep.gamma) + n, g8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = round_t<T>(v[e] + b8[e]);   // attention branch p, as stored
+          w[e] = xv[e] + pv[e];               // x' (Eq. 5) in fp32: LayerNorm 2 statistics
+          u[e] = w[e] * g8[e];                // x' * gamma2: fc1's A operand
+        }
+        store8f(out + (size_t)m * ep.ldo + n, pv);
+        store8f(static_cast<T*>(ep.out2) + (size_t)m * N + n, u);
+      } else {
+        frag_to_f32(pp[pass], pv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = v[e] + b8[e];   // MLP(LN(x'))
           const float xp = xv[e] + pv[e]; // x' (Eq. 5), re-formed in fp32
           const float d = y - xp;
-          ss += d * d;
-          v[e] = xp + y;                  // x_hat (Eq. 6)
+          sdev += d * d;
+          w[e] = round_t<T>(xp + y);      // x_hat (Eq. 6), as stored
         }
-        store8f(out + (size_t)m * ep.ldo + n, v);
+        store8f(out + (size_t)m * ep.ldo + n, w);
       }
-      if (ep.part) {
-        // 8 lanes cover one 64-column wave slice of the row: one partial per slice
-        ss += __shfl_xor(ss, 4, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        ss += __shfl_xor(ss, 1, 64);
-        if ((tid & 7) == 0 && m < M) ep.part[(size_t)m * ep.nparts + nt * 2 + ((tid >> 3) & 1)] = ss;
-      }
-    } else if (ok) {
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[e] += b8[e];
-        if (EPI == kEpiGelu) v[e] = gelu_t<T>(v[e]);
-      }
-      store8f(out + (size_t)m * ep.ldo + n, v);
+      for (int e = 0; e < 8; ++e) w[e] = 0.f;
+    }
+    // slice partials of the stored row values (8 lanes = one 64-column slice)
+    float ssum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ssum += w[e];
+    const float smean = sum8(ssum) * (1.0f / 64.0f);
+    float sm2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dd = w[e] - smean;
+      sm2 += dd * dd;
+    }
+    sm2 = sum8(sm2);
+    if ((sub & 7) == 0 && row_ok && slice < nsl && ep.stats_out) {
+      float* so = ep.stats_out + ((size_t)m * e_stride + slice) * 2;
+      so[0] = smean;
+      so[1] = sm2;
+    }
+    if (EPI == kEpiFc2 && ep.part) {
+      sdev = sum8(sdev);
+      if ((sub & 7) == 0 && row_ok) ep.part[(size_t)m * ep.nparts + slice] = sdev;
     }
   }
 }
@@ -278,7 +389,7 @@ hipError_t launch_cfg(GemmEpilogue epi, const void* A, const void* W, int M, int
   const T* w = static_cast<const T*>(W);
   switch (epi) {
     case kEpiQKV: gemm_kernel<T, kEpiQKV, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiBias: gemm_kernel<T, kEpiBias, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiProj: gemm_kernel<T, kEpiProj, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
     case kEpiGelu: gemm_kernel<T, kEpiGelu, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
     case kEpiFc2: gemm_kernel<T, kEpiFc2, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
   }

@@ -18,11 +18,19 @@ inline int score_parts(int C) { return 2 * ((C + kGemmTile - 1) / kGemmTile); }
 // Padded key length of the transposed V buffer (whole 64-key tiles).
 inline int padded_len(int L) { return (L + 63) / 64 * 64; }
 
+// LayerNorm is folded into the GEMM that consumes it:
+//   LN(z) W^T + b = rstd * (z W'^T - mu * c) + d,  W' = W diag(gamma), c = W' 1, d = W beta + b
+// Row statistics travel as partials over 64-column slices: (slice mean, slice sum of squared
+// deviations from it), merged exactly by the consumer.  A row of partials is padded to an
+// even number of slices (16-byte rows).
+__host__ __device__ inline int stat_slices(int C) { return C / 64; }
+__host__ __device__ inline int stat_stride(int C) { return (C / 64 + 1) / 2 * 2; }  // float2 per row
+
 enum GemmEpilogue {
-  kEpiQKV = 0,   // + b_qkv; Q|K -> qk [M][2C]; V -> vt [B][H][64][Lp] (transposed per head)
-  kEpiBias = 1,  // + bias -> out [M][N]                          (attention projection)
-  kEpiGelu = 2,  // GELU(+ bias) -> out [M][N]                      (fc1)
-  kEpiFc2 = 3    // y = acc + b2; out = (x + p) + y; part += sum((y - (x + p))^2)
+  kEpiQKV = 0,   // LN1 folded; Q|K -> qk [M][2C]; V -> vt [B][H][64][Lp] (transposed per head)
+  kEpiProj = 1,  // p = acc + b -> out; x' = x + p -> out2; LN2 slice partials of x' -> stats_out
+  kEpiGelu = 2,  // LN2 folded, GELU -> out [M][N]                 (fc1)
+  kEpiFc2 = 3    // y = acc + b2; out = (x + p) + y; score partials; LN1 slice partials of out
 };
 
 struct GemmEpiArgs {
@@ -32,20 +40,46 @@ struct GemmEpiArgs {
   // kEpiQKV: output columns >= vcol0 (= 2C, a multiple of the tile width) are V
   void* vt = nullptr;
   int vcol0 = 0, L = 1, Lp = 64, heads = 1;
-  // kEpiFc2: x' = x + p is re-formed in fp32 from the block input and the attention branch
+  // kEpiProj / kEpiFc2: x' = x + p is re-formed in fp32 from the block input and the
+  // attention branch
   const void* x = nullptr;
   const void* p = nullptr;
+  void* out2 = nullptr;        // kEpiProj: x' * gamma2 in the storage type (fc1's A operand)
+  const void* gamma = nullptr; // kEpiProj: LayerNorm 2 gamma [N]
   float* part = nullptr;       // [M][nparts] or null (no scoring)
   int nparts = 0;
+  // folded LayerNorm of the A operand rows (kEpiQKV, kEpiGelu)
+  const float* stats_in = nullptr;  // [M][stat_stride] float2 slice partials
+  const float* fold_c = nullptr;    // [N]
+  const float* fold_d = nullptr;    // [N]
+  float eps = 1e-6f;
+  int C = 0;                        // LayerNorm width (= K of the consuming GEMM)
+  // slice partials of the output rows (kEpiProj: of x'; kEpiFc2: of x_hat)
+  float* stats_out = nullptr;
 };
 
 // Y = A W^T (+ epilogue).  A [M][K], W [N][K]; K % 64 == 0 (bf16) / % 32 (f32).
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
                        int K, const GemmEpiArgs& ep, hipStream_t stream);
 
-// out = LN(x (+ p)) over C per row; p nullable.  C % 8 == 0, C <= 1024.
-hipError_t launch_layernorm(Dtype dt, const void* x, const void* p, const void* g, const void* b,
-                            float eps, void* out, int M, int C, hipStream_t stream);
+// Slice partials of every row of x [M][C] -> stats [M][stat_stride(C)] float2.
+hipError_t launch_row_stats(Dtype dt, const void* x, float* stats, int M, int C, hipStream_t stream);
+
+// One weight to fold: W [rows][C] with the LayerNorm gamma/beta [C] and Linear bias [rows]
+// -> c [rows], d [rows] (fp32) and, if w_out is not null, W' = W diag(gamma) [rows][C] in
+// the storage type with c = W' 1 (else c = W gamma).
+struct FoldJob {
+  const void* w;
+  const void* gamma;
+  const void* beta;
+  const void* bias;
+  void* w_out;
+  float* c;
+  float* d;
+  int rows;
+};
+constexpr int kMaxFoldJobs = 8;
+hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStream_t stream);
 
 // Fused attention, one (sample, head, 64-query block) per workgroup.
 // qk [B*L][2C] (Q at columns h*64.., K at C + h*64..), vt [B][H][64][Lp] -> out [B*L][C].

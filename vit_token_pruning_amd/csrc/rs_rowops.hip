@@ -1,5 +1,6 @@
-// Row-wise and selection kernels: LayerNorm, the standalone representation-shift score,
-// the per-sample exact top-k, and the compaction of kept rows.
+// Row-wise and selection kernels: LayerNorm preparation (row statistics, folded weights),
+// the standalone representation-shift score, the per-sample exact top-k, and the
+// compaction of kept rows.
 //
 // Method: "Representation Shift: Unifying Token Compression with FlashAttention" (arXiv
 // HTML).  LayerNorm is the LN of Sec. 3.3, Eqs. (5) and (6); the score is Eq. (4) with
@@ -12,58 +13,89 @@
 namespace rs {
 namespace {
 
-// ---------------------------------------------------------------- LayerNorm
-// One wave per row; each lane holds up to two 8-element chunks (C <= 1024).
-// Statistics in fp32: mean, then the biased variance around it.
+// ---------------------------------------------------------------- LayerNorm preparation
+// LayerNorm (Sec. 3.3) runs folded into the GEMM that consumes it (see rs_gemm.hip); these
+// two kernels prepare it: the slice statistics of a block input that no GEMM epilogue
+// produced (the encoder's first block), and the folded weights W' = W diag(gamma),
+// c = W' 1, d = W beta + b.
+
+// One wave per row; lane ch handles 8-element chunk ch (and ch + 64), so the 8 lanes
+// 8s..8s+7 of an iteration hold slice s: its mean, then the sum of squared deviations.
 template <typename T>
-__global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
-                                                        const T* __restrict__ p,
-                                                        const T* __restrict__ gam,
-                                                        const T* __restrict__ bet, float eps,
-                                                        T* __restrict__ out, int M, int C) {
+__global__ __launch_bounds__(256) void row_stats_kernel(const T* __restrict__ x,
+                                                        float* __restrict__ stats, int M, int C) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;  // whole wave
-  const int nch = C >> 3;
-  const size_t base = (size_t)row * C;
-  float v[2][8];
-  float s = 0.f;
+  const int nch = C >> 3, stride = stat_stride(C);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int ch = lane + it * 64;
+    if (it * 64 >= nch) break;  // uniform
+    float v[8];
     if (ch < nch) {
-      load8f(x + base + ch * 8, v[it]);
-      if (p) {
-        float q[8];
-        load8f(p + base + ch * 8, q);
+      load8f(x + (size_t)row * C + ch * 8, v);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[it][e] += q[e];
-      }
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[it][e];
+    for (int e = 0; e < 8; ++e) s += v[e];
+    const float mean = sum8(s) * (1.0f / 64.0f);
+    float m2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mean;
+      m2 += d * d;
+    }
+    m2 = sum8(m2);
+    if ((ch & 7) == 0 && ch < nch) {
+      float* so = stats + ((size_t)row * stride + (ch >> 3)) * 2;
+      so[0] = mean;
+      so[1] = m2;
     }
   }
-  const float mean = wave_sum(s) / (float)C;
-  float s2 = 0.f;
+}
+
+struct FoldArgs {
+  FoldJob job[kMaxFoldJobs];
+  int rows_before[kMaxFoldJobs + 1];  // prefix sum of job rows
+  int njobs;
+  int C;
+};
+
+// One wave per output row n of one job: W'[n][k] = W[n][k] * gamma[k] (rounded to the
+// storage type; only if the job has an output), c[n] = sum_k W'[n][k] (or the unrounded
+// sum_k W[n][k] gamma[k]), d[n] = sum_k W[n][k] beta[k] + b[n].
+template <typename T>
+__global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= fa.rows_before[fa.njobs]) return;  // whole wave
+  int j = 0;
+  while (j + 1 < fa.njobs && r >= fa.rows_before[j + 1]) ++j;
+  const FoldJob& jb = fa.job[j];
+  const int n = r - fa.rows_before[j], C = fa.C, nch = C >> 3;
+  const T* w = static_cast<const T*>(jb.w) + (size_t)n * C;
+  T* wo = jb.w_out ? static_cast<T*>(jb.w_out) + (size_t)n * C : nullptr;
+  float c = 0.f, d = 0.f;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float wv[8], g[8], b[8], o[8];
+    load8f(w + ch * 8, wv);
+    load8f(static_cast<const T*>(jb.gamma) + ch * 8, g);
+    load8f(static_cast<const T*>(jb.beta) + ch * 8, b);
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
-    if (lane + it * 64 < nch)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[it][e] - mean;
-        s2 += d * d;
-      }
-  const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)C + eps);
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int ch = lane + it * 64;
-    if (ch < nch) {
-      float gg[8], bb[8], o[8];
-      load8f(gam + ch * 8, gg);
-      load8f(bet + ch * 8, bb);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (v[it][e] - mean) * rstd * gg[e] + bb[e];
-      store8f(out + base + ch * 8, o);
+    for (int e = 0; e < 8; ++e) {
+      o[e] = wo ? round_t<T>(wv[e] * g[e]) : wv[e] * g[e];
+      c += o[e];
+      d = fmaf(wv[e], b[e], d);
     }
+    if (wo) store8f(wo + ch * 8, o);
+  }
+  c = wave_sum(c);
+  d = wave_sum(d);
+  if (lane == 0) {
+    jb.c[n] = c;
+    jb.d[n] = d + to_f32(static_cast<const T*>(jb.bias)[n]);
   }
 }
 
@@ -252,17 +284,29 @@ int grid_for(long long units) {
 
 }  // namespace
 
-hipError_t launch_layernorm(Dtype dt, const void* x, const void* p, const void* g, const void* b,
-                            float eps, void* out, int M, int C, hipStream_t stream) {
+hipError_t launch_row_stats(Dtype dt, const void* x, float* stats, int M, int C, hipStream_t stream) {
   const int grid = (M + 3) / 4;
   if (dt == kBF16)
-    layernorm_kernel<bf16><<<grid, 256, 0, stream>>>(
-        static_cast<const bf16*>(x), static_cast<const bf16*>(p), static_cast<const bf16*>(g),
-        static_cast<const bf16*>(b), eps, static_cast<bf16*>(out), M, C);
+    row_stats_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(x), stats, M, C);
   else
-    layernorm_kernel<float><<<grid, 256, 0, stream>>>(
-        static_cast<const float*>(x), static_cast<const float*>(p), static_cast<const float*>(g),
-        static_cast<const float*>(b), eps, static_cast<float*>(out), M, C);
+    row_stats_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), stats, M, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStream_t stream) {
+  FoldArgs fa;
+  fa.njobs = njobs;
+  fa.C = C;
+  fa.rows_before[0] = 0;
+  for (int j = 0; j < njobs; ++j) {
+    fa.job[j] = jobs[j];
+    fa.rows_before[j + 1] = fa.rows_before[j] + jobs[j].rows;
+  }
+  const int grid = (fa.rows_before[njobs] + 3) / 4;
+  if (dt == kBF16)
+    fold_kernel<bf16><<<grid, 256, 0, stream>>>(fa);
+  else
+    fold_kernel<float><<<grid, 256, 0, stream>>>(fa);
   return hipGetLastError();
 }
 
