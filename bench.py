@@ -62,7 +62,8 @@ def cpu_baseline(wl, x, blocks, budget_s=12.0):
 # device kernel symbol (mangled) -> kernel class of the library's timing interface
 def kernel_class(mangled: str):
     import re
-    m = re.search(r"gemm_kernelI(DF16b|f)Li(\d)E", mangled)
+    # the GEMM and, when K is split, its reduction kernel (which runs the epilogue)
+    m = re.search(r"(?:gemm_kernel|splitk_reduce_kernel)I(DF16b|f)Li(\d)E", mangled)
     if m:
         return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score"}[m.group(2)]
     for key, name in (("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),

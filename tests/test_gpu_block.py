@@ -18,6 +18,15 @@ CASES += [("deit_s", 3, L, 0.7) for L in (197, 138, 97, 68)]
 CASES += [("deit_b", 2, L, 0.65) for L in (197, 128, 83, 54)]
 CASES += [("umt_b", 1, L, 0.5) for L in (1568, 784, 392, 196)]
 CASES += [("umt_l", 1, L, 0.5) for L in (1568, 784, 392, 196, 98)]
+# fp32 with K split (fc2 at DeiT-S widths; all four GEMMs at UMT-L widths)
+CASES += [("deit_s@f32", 2, 97, 0.7), ("umt_l@f32", 1, 98, 0.5)]
+
+
+def _wl(name):
+    """A workload by name; `name@f32` is the same architecture computed in fp32."""
+    import dataclasses
+    base, _, dt = name.partition("@")
+    return dataclasses.replace(W[base], dtype=dt) if dt else W[base]
 
 
 def _block(wl, B, L, k, init, seed, zero=(), spread=False):
@@ -36,7 +45,7 @@ def _block(wl, B, L, k, init, seed, zero=(), spread=False):
 @pytest.mark.parametrize("init", ["full", "paper"])
 def test_block_matches_oracle(name, B, L, ratio, init):
     import vit_token_pruning_amd as rs
-    wl = W[name]
+    wl = _wl(name)
     k = O.keep_count(ratio, L)
     seed = 11 + L
     x, w, r = _block(wl, B, L, k, init, seed)

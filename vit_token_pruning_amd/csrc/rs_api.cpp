@@ -146,6 +146,7 @@ struct BlockWs {
   float* st_x;    // slice partials of the block input rows (LayerNorm 1)
   float* st_xp;   // slice partials of x' rows (LayerNorm 2)
   float* st_xhat; // slice partials of x_hat rows (next block's LayerNorm 1)
+  float* split;   // split-K partial tiles (rs::kSplitWsBytes)
 };
 struct FoldWs {   // LayerNorm folding of one block: W_qkv diag(gamma1); c, d of QKV and fc1
   void* wq;
@@ -165,7 +166,7 @@ size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
 size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws) {
   const size_t e = esize(d.dtype), M = (size_t)B * L, C = d.C;
   const size_t st = M * rs::stat_stride(d.C) * 8;
-  const size_t sizes[11] = {
+  const size_t sizes[12] = {
       M * 2 * C * e,                                     // qk: Q | K
       (size_t)B * d.heads * 64 * rs::padded_len(L) * e,  // vt: V^T per head
       M * C * e,                                         // o: attention output
@@ -175,14 +176,16 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
       M * C * e,                                         // xhat: block output
       M * (size_t)rs::score_parts(d.C) * 4,              // part: score partials
       st, st, st,                                        // slice partials
+      rs::kSplitWsBytes,                                 // split-K partial tiles
   };
-  void* p[11];
-  const size_t off = carve_seq(base, sizes, 11, p);
+  void* p[12];
+  const size_t off = carve_seq(base, sizes, 12, p);
   if (ws) {
     ws->qk = p[0]; ws->vt = p[1]; ws->o = p[2]; ws->p = p[3]; ws->xp = p[4]; ws->h = p[5];
     ws->xhat = p[6]; ws->part = static_cast<float*>(p[7]);
     ws->st_x = static_cast<float*>(p[8]); ws->st_xp = static_cast<float*>(p[9]);
     ws->st_xhat = static_cast<float*>(p[10]);
+    ws->split = static_cast<float*>(p[11]);
   }
   return off;
 }
@@ -285,6 +288,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     ep.out = ws.qk; ep.ldo = 2 * C;
     ep.vt = ws.vt; ep.vcol0 = 2 * C; ep.L = L; ep.Lp = rs::padded_len(L); ep.heads = d.heads;
     ep.stats_in = st_x; ep.fold_c = fw.cq; ep.fold_d = fw.dq; ep.eps = d.ln_eps; ep.C = C;
+    ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_QKV, 2.0 * Md * 3 * Cd * Cd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiQKV, x, fw.wq, M, 3 * C, C, ep, st);
     }));
@@ -296,6 +300,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
     ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
+    ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiProj, ws.o, w.w_proj, M, C, C, ep, st);
     }));
@@ -304,6 +309,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     rs::GemmEpiArgs ep;
     ep.out = ws.h; ep.ldo = Hd;
     ep.stats_in = ws.st_xp; ep.fold_c = fw.c1; ep.fold_d = fw.d1; ep.eps = d.ln_eps; ep.C = C;
+    ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_FC1, 2.0 * Md * Cd * Hd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiGelu, ws.xp, w.w_fc1, M, Hd, C, ep, st);
     }));
@@ -313,6 +319,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
     ep.x = x; ep.p = ws.p; ep.part = part; ep.nparts = rs::score_parts(C);
     ep.stats_out = st_out; ep.C = C;
+    ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
     }));

@@ -72,186 +72,65 @@ struct Tile {
   static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "loader must divide evenly");
 };
 
-template <typename T, int EPI, class G>
-__global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
-                                                     const T* __restrict__ W, int M, int N,
-                                                     int K, GemmEpiArgs ep) {
-  constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
-  constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
-  // pipeline stages, or the staged fp32 tile plus one float2 per tile row
-  constexpr int SMEM = 2 * STAGE > G::BM * kCS * 4 + G::BM * 8 ? 2 * STAGE : G::BM * kCS * 4 + G::BM * 8;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
-  const int t = xcd_contiguous(blockIdx.x, nM * nN);
-  const int mt = t / nN, nt = t - mt * nN;
-  const int m0 = mt * G::BM, n0 = nt * G::BN;
-  const int wm = wave % G::WM, wn = wave / G::WM;
-
-  // ---- loader: this thread's chunks of A and W, and their swizzled LDS slots
-  const int lc = tid % KC, lr = tid / KC;
-  const char* ag[NA];
-  const char* wg[NW];
-  int sa[NA], sw[NW];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int r = lr + i * RSTEP;
-    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + lc * CB;
-    sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
-  }
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int r = lr + i * RSTEP;
-    wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + lc * CB;
-    sw[i] = ABYTES + r * ROWB + ((lc ^ (r % KC)) * CB);
-  }
-  Frag8<T> ra[PF][NA], rw[PF][NW];
-  auto gload = [&](int kt, int slot) {
-    const size_t off = (size_t)kt * ROWB;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) load_frag(ra[slot][i], ag[i] + off);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) load_frag(rw[slot][i], wg[i] + off);
-  };
-  auto sstore = [&](int slot, int buf) {
-    char* s = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) store_frag(s + sa[i], ra[slot][i]);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) store_frag(s + sw[i], rw[slot][i]);
-  };
-
-  f32x4 acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int buf) {
-    const char* As = smem + buf * STAGE;
-    const char* Ws = As + ABYTES;
-#pragma unroll
-    for (int ks = 0; ks < KC / 4; ++ks) {
-      const int c = ks * 4 + g;
-      Frag8<T> fa[TM], fw[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * TM * 16 + i * 16 + l16;
-        load_frag(fa[i], As + r * ROWB + ((c ^ (r % KC)) * CB));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * TN * 16 + j * 16 + l16;
-        load_frag(fw[j], Ws + r * ROWB + ((c ^ (r % KC)) * CB));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[j][i] = mma16(acc[j][i], fw[j], fa[i]);
-    }
-  };
-
-  const int KT = K / (8 * KC);
-  {
-    gload(0, 0);
-    sstore(0, 0);
-    if (PF > 1 && KT > 1) gload(1, 1 % PF);
-    __syncthreads();
-    // One stage.  PF == 2: the next stage's registers arrived during the previous stage,
-    // so they are written to the free LDS buffer first and those writes overlap this
-    // stage's matrix work; then loads two stages ahead are issued.  PF == 1: loads one
-    // stage ahead, written to LDS after the matrix work.
-    auto step = [&](int kt, auto ls, auto ss) {
-      if (PF > 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
-      if (kt + PF < KT) gload(kt + PF, decltype(ls)::value);
-      compute(kt & 1);
-      if (PF == 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
-      __syncthreads();
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1 % PF>;
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-      // PF == 2: stage kt -> slot 0 (loaded into for kt + 2), stored from slot 1;
-      // PF == 1: single slot
-      step(kt, I0{}, I1{});
-      step(kt + 1, I1{}, I0{});
-    }
-    if (kt < KT) step(kt, I0{}, I1{});
-  }
-
-  // ---------------------------------------------------------------- epilogues
-  // Epilogue inputs from global memory (row statistics, x, p) for all of this thread's
-  // rows are requested here, before the tile is staged, so their latency overlaps the
-  // staging instead of being paid once per row pass.
+// The epilogue of one 128 x 128 output tile, shared by the direct path and the split-K
+// reduction.  `stage(Cs, vtile)` writes the tile's fp32 accumulators to LDS -- Cs[m][n]
+// for the row-wise epilogues, Cs[n][m] for the V columns of QKV -- with every LDS byte
+// free when it is called.
+template <typename T, int EPI, class G, class Stage>
+__device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep, int M, int N,
+                                              int m0, int n0, int nt, Stage&& stage) {
+  static_assert(G::BM == 128 && G::BN == 128 && G::NT == 256, "epilogue assumes 128x128, 256 threads");
   constexpr int NPASS = G::BM / 16;
-  constexpr bool kFoldE = EPI == kEpiQKV || EPI == kEpiGelu;
+  constexpr bool kFold = EPI == kEpiQKV || EPI == kEpiGelu;   // LayerNorm folded into A
   constexpr bool kResid = EPI == kEpiProj || EPI == kEpiFc2;
-  const int e_er = tid >> 4, e_sub = tid & 15, e_n = n0 + e_sub * 8;
-  const int e_nsl = stat_slices(ep.C), e_stride = stat_stride(ep.C);
-  const bool e_vt = EPI == kEpiQKV && n0 >= ep.vcol0;
-  // kFoldE: thread t < 128 fetches all slice partials of tile row t (at most 16)
+  const int tid = threadIdx.x;
+  const int er = tid >> 4, sub = tid & 15, ec = sub * 8;       // row pass: 16 threads per row
+  const int n = n0 + ec;
+  const bool col_ok = n < N;
+  const int nsl = stat_slices(ep.C), sstride = stat_stride(ep.C);
+  const bool vtile = EPI == kEpiQKV && n0 >= ep.vcol0;         // uniform per workgroup
+
+  // Epilogue inputs from global memory (row statistics, x, p) for all of this thread's
+  // rows are requested before the tile is staged, so their latency overlaps the staging
+  // instead of being paid once per row pass.
+  // kFold: thread t < 128 fetches all slice partials of tile row t (at most 16)
   float2 rpart[16];
-  if (kFoldE && tid < G::BM) {
+  if (kFold && tid < G::BM) {
     const int m = m0 + tid;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       rpart[q] = make_float2(0.f, 0.f);
-      if (q < e_nsl && m < M)
-        rpart[q] = *reinterpret_cast<const float2*>(ep.stats_in + ((size_t)m * e_stride + q) * 2);
+      if (q < nsl && m < M)
+        rpart[q] = *reinterpret_cast<const float2*>(ep.stats_in + ((size_t)m * sstride + q) * 2);
     }
   }
   Frag8<T> px[NPASS], pp[NPASS];           // kResid: x (and p) of each row
-  if (!e_vt) {
+  if (kResid) {
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-      const int m = m0 + pass * 16 + e_er;
-      if (kResid && m < M && e_n < N) {
-        load_frag(px[pass], static_cast<const T*>(ep.x) + (size_t)m * N + e_n);
-        if (EPI == kEpiFc2) load_frag(pp[pass], static_cast<const T*>(ep.p) + (size_t)m * N + e_n);
+      const int m = m0 + pass * 16 + er;
+      if (m < M && col_ok) {
+        load_frag(px[pass], static_cast<const T*>(ep.x) + (size_t)m * N + n);
+        if (EPI == kEpiFc2) load_frag(pp[pass], static_cast<const T*>(ep.p) + (size_t)m * N + n);
       }
     }
   }
 
-  // The fp32 tile is staged in LDS (the pipeline buffers are free after the last
-  // barrier): Cs[m][n] for row-wise epilogues, Cs[n][m] for the V columns of QKV.
-  // acc[j][i] = D[n][m]: lane holds row m, columns n..n+3.
-  static_assert(G::BM == 128 && G::BN == 128 && G::NT == 256, "epilogue assumes 128x128, 256 threads");
   float* Cs = reinterpret_cast<float*>(smem);
-  const bool vtile = EPI == kEpiQKV && n0 >= ep.vcol0;  // uniform per workgroup
-  if (vtile) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Cs[(n + v) * kCS + m] = acc[j][i][v];
-      }
-  } else {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
-        *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
-      }
-  }
+  stage(Cs, vtile);
+
   // folded LayerNorm: each tile row's (mean * rstd, rstd), merged once from its slice
   // partials (equal-count merge) and shared through LDS
   float2* Rs = reinterpret_cast<float2*>(smem + G::BM * kCS * 4);
-  if (kFoldE && tid < G::BM) {
+  if (kFold && tid < G::BM) {
     float mean = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) mean += rpart[q].x;  // absent slices hold 0
-    mean /= (float)e_nsl;
+    mean /= (float)nsl;
     float m2 = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      if (q < e_nsl) {
+      if (q < nsl) {
         const float dm = rpart[q].x - mean;
         m2 += rpart[q].y + 64.f * dm * dm;
       }
@@ -260,9 +139,6 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   }
   __syncthreads();
 
-  const T* bias = static_cast<const T*>(ep.bias);
-  constexpr bool kFold = kFoldE;  // LayerNorm folded into A
-  const int nsl = e_nsl;
   if (vtile) {
     // V^T [b][h][d][token]: a wave writes 64 consecutive tokens of one channel per store
     T* vt = static_cast<T*>(ep.vt);
@@ -274,21 +150,18 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
       T* vrow = vt + (size_t)bb * ep.heads * 64 * ep.Lp + tk;
 #pragma unroll 4
       for (int jj = 0; jj < 64; ++jj) {
-        const int nn = half * 64 + jj, n = n0 + nn;
-        if (n < N) {
-          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, ep.fold_c[n], ep.fold_d[n]));
-          vrow[(size_t)(n - ep.vcol0) * ep.Lp] = from_f32<T>(v);
+        const int nn = half * 64 + jj, nc = n0 + nn;
+        if (nc < N) {
+          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, ep.fold_c[nc], ep.fold_d[nc]));
+          vrow[(size_t)(nc - ep.vcol0) * ep.Lp] = from_f32<T>(v);
         }
       }
     }
     return;
   }
 
-  // row pass: 16 threads per row, 8 consecutive columns each; lanes 0-7 / 8-15 of a row
-  // cover its two 64-column slices of this tile
-  const int er = tid >> 4, sub = tid & 15, ec = sub * 8;
-  const int n = n0 + ec;
-  const bool col_ok = n < N;
+  // row pass: 8 consecutive columns per thread; lanes 0-7 / 8-15 of a row cover its two
+  // 64-column slices of this tile
   const int slice = nt * 2 + (sub >> 3);          // 64-column slice of the row
   float b8[8], c8[8], d8[8];
   if (kFold) {
@@ -297,7 +170,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
       for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
     }
   } else if (col_ok) {
-    load8f(bias + n, b8);
+    load8f(static_cast<const T*>(ep.bias) + n, b8);
   }
   T* out = static_cast<T*>(ep.out);
 #pragma unroll
@@ -370,7 +243,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     }
     sm2 = sum8(sm2);
     if ((sub & 7) == 0 && row_ok && slice < nsl && ep.stats_out) {
-      float* so = ep.stats_out + ((size_t)m * e_stride + slice) * 2;
+      float* so = ep.stats_out + ((size_t)m * sstride + slice) * 2;
       so[0] = smean;
       so[1] = sm2;
     }
@@ -381,19 +254,251 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   }
 }
 
-template <typename T, class G>
-hipError_t launch_cfg(GemmEpilogue epi, const void* A, const void* W, int M, int N, int K,
-                      const GemmEpiArgs& ep, hipStream_t st) {
+// SPLIT == false: one workgroup per output tile over all of K, then the tile epilogue.
+// SPLIT == true: `splits` workgroups per tile, each over one contiguous range of K stages,
+// writing its fp32 partial tile to ep.split_ws [split][M][N]; splitk_reduce_kernel finishes.
+// Launch ids are spread XCD-contiguously, and in split mode the splits of one tile are
+// neighbours, so a tile's partials and its reduction share an XCD's L2.
+template <typename T, int EPI, class G, bool SPLIT>
+__global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
+                                                     const T* __restrict__ W, int M, int N,
+                                                     int K, int splits, GemmEpiArgs ep) {
+  constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
+  constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
+  // pipeline stages, or the staged fp32 tile plus one float2 per tile row
+  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + G::BM * 8;
+  constexpr int SMEM = 2 * STAGE > EBYTES ? 2 * STAGE : EBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
+  const int KTall = K / (8 * KC);
+  int t, split = 0, kt0 = 0, KT = KTall;
+  if (SPLIT) {
+    const int u = xcd_contiguous(blockIdx.x, nM * nN * splits);
+    t = u / splits;
+    split = u - t * splits;
+    kt0 = split * KTall / splits;
+    KT = (split + 1) * KTall / splits - kt0;
+  } else {
+    t = xcd_contiguous(blockIdx.x, nM * nN);
+  }
+  const int mt = t / nN, nt = t - mt * nN;
+  const int m0 = mt * G::BM, n0 = nt * G::BN;
+  const int wm = wave % G::WM, wn = wave / G::WM;
+
+  // ---- loader: this thread's chunks of A and W, and their swizzled LDS slots
+  const int lc = tid % KC, lr = tid / KC;
+  const char* ag[NA];
+  const char* wg[NW];
+  int sa[NA], sw[NW];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int r = lr + i * RSTEP;
+    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + lc * CB;
+    sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
+  }
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int r = lr + i * RSTEP;
+    wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + (size_t)kt0 * ROWB + lc * CB;
+    sw[i] = ABYTES + r * ROWB + ((lc ^ (r % KC)) * CB);
+  }
+  Frag8<T> ra[PF][NA], rw[PF][NW];
+  auto gload = [&](int kt, int slot) {
+    const size_t off = (size_t)kt * ROWB;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_frag(ra[slot][i], ag[i] + off);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) load_frag(rw[slot][i], wg[i] + off);
+  };
+  auto sstore = [&](int slot, int buf) {
+    char* s = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) store_frag(s + sa[i], ra[slot][i]);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) store_frag(s + sw[i], rw[slot][i]);
+  };
+
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    const char* As = smem + buf * STAGE;
+    const char* Ws = As + ABYTES;
+#pragma unroll
+    for (int ks = 0; ks < KC / 4; ++ks) {
+      const int c = ks * 4 + g;
+      Frag8<T> fa[TM], fw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 16 + i * 16 + l16;
+        load_frag(fa[i], As + r * ROWB + ((c ^ (r % KC)) * CB));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 16 + j * 16 + l16;
+        load_frag(fw[j], Ws + r * ROWB + ((c ^ (r % KC)) * CB));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[j][i] = mma16(acc[j][i], fw[j], fa[i]);
+    }
+  };
+
+  {
+    gload(0, 0);
+    sstore(0, 0);
+    if (PF > 1 && KT > 1) gload(1, 1 % PF);
+    __syncthreads();
+    // One stage.  PF == 2: the next stage's registers arrived during the previous stage,
+    // so they are written to the free LDS buffer first and those writes overlap this
+    // stage's matrix work; then loads two stages ahead are issued.  PF == 1: loads one
+    // stage ahead, written to LDS after the matrix work.
+    auto step = [&](int kt, auto ls, auto ss) {
+      if (PF > 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
+      if (kt + PF < KT) gload(kt + PF, decltype(ls)::value);
+      compute(kt & 1);
+      if (PF == 1 && kt + 1 < KT) sstore(decltype(ss)::value, (kt + 1) & 1);
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % PF>;
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      // PF == 2: stage kt -> slot 0 (loaded into for kt + 2), stored from slot 1;
+      // PF == 1: single slot
+      step(kt, I0{}, I1{});
+      step(kt + 1, I1{}, I0{});
+    }
+    if (kt < KT) step(kt, I0{}, I1{});
+  }
+
+  // acc[j][i] = D[n][m]: lane holds row m, columns n..n+3
+  if (SPLIT) {
+    // partial tile straight from registers: 16-byte stores, 64 contiguous bytes per row
+    float* ps = ep.split_ws + (size_t)split * M * N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * TM * 16 + i * 16 + l16, n = n0 + wn * TN * 16 + j * 16 + 4 * g;
+        if (m < M && n < N) *reinterpret_cast<f32x4*>(ps + (size_t)m * N + n) = acc[j][i];
+      }
+    return;
+  }
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, bool vtile) {
+    if (vtile) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Cs[(n + v) * kCS + m] = acc[j][i][v];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
+          *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
+        }
+    }
+  });
+}
+
+// Split-K reduction: one workgroup per output tile sums the `splits` partial tiles in
+// split order (a fixed order, so the result is deterministic) into LDS and runs the same
+// tile epilogue as the direct path.
+template <typename T, int EPI, class G>
+__global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int splits, GemmEpiArgs ep) {
+  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + G::BM * 8];
+  constexpr int NPASS = G::BM / 16;
+  const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
+  const int t = xcd_contiguous(blockIdx.x, nM * nN);
+  const int mt = t / nN, nt = t - mt * nN;
+  const int m0 = mt * G::BM, n0 = nt * G::BN;
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, bool vtile) {
+    const int tid = threadIdx.x, er = tid >> 4, ec = (tid & 15) * 8;
+    // Rows and columns past the matrix edge read a clamped, written element instead of
+    // branching, so a split's 16 loads per thread are all in flight together; the
+    // epilogue never uses those LDS entries.
+    const size_t ncl = (size_t)min(n0 + ec, N - 8);
+    size_t off[NPASS];
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass)
+      off[pass] = (size_t)min(m0 + pass * 16 + er, M - 1) * N + ncl;
+    f32x4 a[NPASS][2];
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) a[pass][0] = a[pass][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const size_t sstep = (size_t)M * N;
+    const float* ps = ep.split_ws;
+    for (int s = 0; s < splits; ++s, ps += sstep) {
+      f32x4 r[NPASS][2];
+#pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
+        r[pass][0] = *reinterpret_cast<const f32x4*>(ps + off[pass]);
+        r[pass][1] = *reinterpret_cast<const f32x4*>(ps + off[pass] + 4);
+      }
+#pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
+        a[pass][0] += r[pass][0];
+        a[pass][1] += r[pass][1];
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int mm = pass * 16 + er;
+      if (vtile) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Cs[(ec + e) * kCS + mm] = a[pass][0][e];
+          Cs[(ec + 4 + e) * kCS + mm] = a[pass][1][e];
+        }
+      } else {
+        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec) = a[pass][0];
+        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec + 4) = a[pass][1];
+      }
+    }
+  });
+}
+
+template <typename T, class G, int EPI>
+hipError_t launch_epi(Dtype dt, const T* a, const T* w, int M, int N, int K, const GemmEpiArgs& ep,
+                      hipStream_t st) {
   const int tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
+  const int S = ep.split_ws ? gemm_splits(dt, M, N, K) : 1;
+  if (S == 1) {
+    gemm_kernel<T, EPI, G, false><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, 1, ep);
+    return hipGetLastError();
+  }
+  gemm_kernel<T, EPI, G, true><<<tiles * S, G::NT, 0, st>>>(a, w, M, N, K, S, ep);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  splitk_reduce_kernel<T, EPI, G><<<tiles, G::NT, 0, st>>>(M, N, S, ep);
+  return hipGetLastError();
+}
+
+template <typename T, class G>
+hipError_t launch_cfg(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N, int K,
+                      const GemmEpiArgs& ep, hipStream_t st) {
   const T* a = static_cast<const T*>(A);
   const T* w = static_cast<const T*>(W);
   switch (epi) {
-    case kEpiQKV: gemm_kernel<T, kEpiQKV, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiProj: gemm_kernel<T, kEpiProj, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiGelu: gemm_kernel<T, kEpiGelu, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
-    case kEpiFc2: gemm_kernel<T, kEpiFc2, G><<<tiles, G::NT, 0, st>>>(a, w, M, N, K, ep); break;
+    case kEpiQKV: return launch_epi<T, G, kEpiQKV>(dt, a, w, M, N, K, ep, st);
+    case kEpiProj: return launch_epi<T, G, kEpiProj>(dt, a, w, M, N, K, ep, st);
+    case kEpiGelu: return launch_epi<T, G, kEpiGelu>(dt, a, w, M, N, K, ep, st);
+    case kEpiFc2: return launch_epi<T, G, kEpiFc2>(dt, a, w, M, N, K, ep, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 // fc2 always runs with 2 waves of 64 columns across a 128-column tile, so the score
@@ -404,8 +509,8 @@ template <typename T> using TileMain = Tile<T, 2, 2, 4, 4, 1>;
 
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
                        int K, const GemmEpiArgs& ep, hipStream_t stream) {
-  if (dt == kBF16) return launch_cfg<bf16, TileMain<bf16>>(epi, A, W, M, N, K, ep, stream);
-  return launch_cfg<float, TileMain<float>>(epi, A, W, M, N, K, ep, stream);
+  if (dt == kBF16) return launch_cfg<bf16, TileMain<bf16>>(dt, epi, A, W, M, N, K, ep, stream);
+  return launch_cfg<float, TileMain<float>>(dt, epi, A, W, M, N, K, ep, stream);
 }
 
 }  // namespace rs

@@ -56,7 +56,41 @@ struct GemmEpiArgs {
   int C = 0;                        // LayerNorm width (= K of the consuming GEMM)
   // slice partials of the output rows (kEpiProj: of x'; kEpiFc2: of x_hat)
   float* stats_out = nullptr;
+  // split-K partial tiles, kSplitWsBytes; null disables splitting
+  float* split_ws = nullptr;
 };
+
+// Split-K.  A GEMM with fewer output tiles than kSplitBelow leaves CUs idle (each tile
+// is one workgroup); it is then cut into S ranges of K: S * tiles workgroups each write
+// an fp32 partial tile, and one reduction workgroup per tile sums the S partials in a
+// fixed order and runs the epilogue.  S * tiles <= kSplitTarget <= kSplitMaxTiles, and
+// every range keeps at least kSplitMinStages K stages.  The choice depends only on
+// (dtype, M, N, K), so equal problems give bit-identical results.
+#ifndef RS_SPLIT_BELOW
+#define RS_SPLIT_BELOW 256
+#endif
+#ifndef RS_SPLIT_TARGET
+#define RS_SPLIT_TARGET 512
+#endif
+#ifndef RS_SPLIT_MIN_STAGES
+#define RS_SPLIT_MIN_STAGES 8
+#endif
+#ifndef RS_SPLIT_MAX
+#define RS_SPLIT_MAX 16
+#endif
+constexpr int kSplitBelow = RS_SPLIT_BELOW, kSplitTarget = RS_SPLIT_TARGET;
+constexpr int kSplitMinStages = RS_SPLIT_MIN_STAGES, kSplitMaxTiles = 512, kSplitMax = RS_SPLIT_MAX;
+static_assert(kSplitTarget <= kSplitMaxTiles, "split buffer is sized for kSplitMaxTiles tiles");
+constexpr size_t kSplitWsBytes = (size_t)kSplitMaxTiles * kGemmTile * kGemmTile * 4;
+inline int gemm_splits(Dtype dt, int M, int N, int K) {
+  const int tiles = ((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+  if (tiles >= kSplitBelow) return 1;
+  const int stages = K / (dt == kBF16 ? 64 : 32);
+  int s = kSplitTarget / tiles;
+  if (s > stages / kSplitMinStages) s = stages / kSplitMinStages;
+  if (s > kSplitMax) s = kSplitMax;
+  return s < 2 ? 1 : s;
+}
 
 // Y = A W^T (+ epilogue).  A [M][K], W [N][K]; K % 64 == 0 (bf16) / % 32 (f32).
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
