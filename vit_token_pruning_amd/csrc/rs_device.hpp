@@ -57,6 +57,27 @@ __device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag8<float>& a, const F
   return acc;
 }
 
+// ---- direct global -> LDS loads ------------------------------------------------------
+// 16 bytes per lane from global memory straight into LDS (no VGPR round trip): lane l's
+// bytes land at lds + 16 l, so one wave writes 1 KiB of consecutive LDS; `lds` must be
+// the same for every lane of the wave.  The builtin exists only for the device target.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+// Wait until at most N of this wave's vector-memory operations are outstanding (loads
+// complete in issue order), leaving the LDS and export counters alone.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes every
+// wave drain all of its in-flight global -> LDS loads first, which would serialize a
+// prefetch pipeline.  Callers wait for the loads they need with wait_vmem<> before
+// arriving, and LDS reads issued before the barrier have been consumed by then.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---- element conversion ------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }

@@ -22,10 +22,11 @@
 // Layout: A [M][K] (activations), W [N][K] (Linear weight, [out][in]); both are
 // K-contiguous.  A workgroup of WM x WN waves computes a (WM*TM*16) x (WN*TN*16) tile,
 // each wave TM x TN MFMA 16x16x32 tiles.  K advances 64 (bf16) or 32 (fp32) elements
-// per LDS stage; LDS is double buffered and global loads run PF stages ahead through
-// registers, so a stage's loads have PF-1 whole stages of matrix work to land behind.
-// LDS rows hold 8 chunks of 8 elements; chunk c of row r sits at slot c ^ (r % chunks)
-// so the 16 rows of a fragment read fall on distinct banks.
+// per LDS stage through two LDS buffers.  bf16 operands go from global memory straight
+// into LDS (16 bytes per lane, no register round trip) one stage ahead of the matrix
+// work; fp32 operands are staged through registers.  LDS rows hold 128 bytes in chunks
+// of 8 elements; chunk c of row r sits at slot c ^ (r % chunks) so 8 consecutive rows
+// of a fragment read fall on distinct banks.
 //
 // Orientation: the weight fragment is the MFMA A operand and the activation fragment
 // the B operand, so a lane ends up holding 4 consecutive output columns of one row.
@@ -288,7 +289,13 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   const int m0 = mt * G::BM, n0 = nt * G::BN;
   const int wm = wave % G::WM, wn = wave / G::WM;
 
-  // ---- loader: this thread's chunks of A and W, and their swizzled LDS slots
+  // ---- loader: this thread's chunks of A and W, and their swizzled LDS slots.  Thread t
+  // moves chunk lc = t % KC of rows lr + i * RSTEP (lr = t / KC).  bf16: each row is 8
+  // chunks of 16 bytes and a wave covers 8 whole rows = 1 KiB of LDS, which is the unit
+  // of the direct global -> LDS load; lane lc then fetches global chunk lc ^ (r % 8) so
+  // that slot lc holds it (the swizzle is an involution).  fp32 (32-byte chunks) goes
+  // through registers.
+  constexpr bool kDirect = sizeof(T) == 2;
   const int lc = tid % KC, lr = tid / KC;
   const char* ag[NA];
   const char* wg[NW];
@@ -296,13 +303,15 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int r = lr + i * RSTEP;
-    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + lc * CB;
+    const int c = kDirect ? (lc ^ (r % KC)) : lc;
+    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + c * CB;
     sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
   }
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int r = lr + i * RSTEP;
-    wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + (size_t)kt0 * ROWB + lc * CB;
+    const int c = kDirect ? (lc ^ (r % KC)) : lc;
+    wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + (size_t)kt0 * ROWB + c * CB;
     sw[i] = ABYTES + r * ROWB + ((lc ^ (r % KC)) * CB);
   }
   Frag8<T> ra[PF][NA], rw[PF][NW];
@@ -319,6 +328,15 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     for (int i = 0; i < NA; ++i) store_frag(s + sa[i], ra[slot][i]);
 #pragma unroll
     for (int i = 0; i < NW; ++i) store_frag(s + sw[i], rw[slot][i]);
+  };
+  // direct: this wave's 1 KiB blocks of stage kt, rows wave * 8 + i * RSTEP ..
+  auto dload = [&](int kt, int buf) {
+    char* s = smem + buf * STAGE;
+    const size_t off = (size_t)kt * ROWB;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_lds16(ag[i] + off, s + (wave * (64 / KC) + i * RSTEP) * ROWB);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) load_lds16(wg[i] + off, s + ABYTES + (wave * (64 / KC) + i * RSTEP) * ROWB);
   };
 
   f32x4 acc[TN][TM];
@@ -352,7 +370,19 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     }
   };
 
-  {
+  if constexpr (kDirect) {
+    // Two LDS buffers; the loads of stage kt + 1 are issued right after the barrier that
+    // ends stage kt - 1 (whose buffer they overwrite) and land during stage kt's matrix work.
+    static_assert(NA + NW > 0 && 64 % KC == 0, "direct loads: whole rows per wave");
+    dload(0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vmem<0>();          // this wave's part of stage kt is in LDS
+      barrier_nofence();       // ... and every wave's; stage kt - 1's reads are done
+      if (kt + 1 < KT) dload(kt + 1, (kt + 1) & 1);
+      compute(kt & 1);
+    }
+    __syncthreads();           // LDS is reused by the epilogue
+  } else {
     gload(0, 0);
     sstore(0, 0);
     if (PF > 1 && KT > 1) gload(1, 1 % PF);
