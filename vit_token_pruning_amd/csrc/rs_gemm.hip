@@ -116,6 +116,21 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       }
     }
   }
+  // per-column constants of this thread's 8 columns (row pass), or of the tile's 128
+  // columns for the V pass (one per thread, handed over through LDS)
+  float b8[8], g8[8], c8[8], d8[8];
+  float2 cdv = make_float2(0.f, 0.f);
+  if (vtile) {
+    if (tid < G::BN && n0 + tid < N) cdv = make_float2(ep.fold_c[n0 + tid], ep.fold_d[n0 + tid]);
+  } else if (col_ok) {
+    if (kFold) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
+    } else {
+      load8f(static_cast<const T*>(ep.bias) + n, b8);
+      if (EPI == kEpiProj) load8f(static_cast<const T*>(ep.gamma) + n, g8);
+    }
+  }
 
   float* Cs = reinterpret_cast<float*>(smem);
   stage(Cs, vtile);
@@ -123,6 +138,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   // folded LayerNorm: each tile row's (mean * rstd, rstd), merged once from its slice
   // partials (equal-count merge) and shared through LDS
   float2* Rs = reinterpret_cast<float2*>(smem + G::BM * kCS * 4);
+  float2* CD = Rs + G::BM;   // V pass: (c, d) of each tile column
   if (kFold && tid < G::BM) {
     float mean = 0.f;
 #pragma unroll
@@ -138,6 +154,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     const float rstd = 1.0f / sqrtf(m2 / (float)ep.C + ep.eps);
     Rs[tid] = make_float2(mean * rstd, rstd);
   }
+  if (vtile && tid < G::BN) CD[tid] = cdv;
   __syncthreads();
 
   if (vtile) {
@@ -149,11 +166,12 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       const float mr = Rs[mm].x, rstd = Rs[mm].y;
       const int bb = m / ep.L, tk = m - bb * ep.L;
       T* vrow = vt + (size_t)bb * ep.heads * 64 * ep.Lp + tk;
-#pragma unroll 4
+#pragma unroll 8
       for (int jj = 0; jj < 64; ++jj) {
         const int nn = half * 64 + jj, nc = n0 + nn;
         if (nc < N) {
-          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, ep.fold_c[nc], ep.fold_d[nc]));
+          const float2 cd = CD[nn];
+          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, cd.x, cd.y));
           vrow[(size_t)(nc - ep.vcol0) * ep.Lp] = from_f32<T>(v);
         }
       }
@@ -164,15 +182,6 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   // row pass: 8 consecutive columns per thread; lanes 0-7 / 8-15 of a row cover its two
   // 64-column slices of this tile
   const int slice = nt * 2 + (sub >> 3);          // 64-column slice of the row
-  float b8[8], c8[8], d8[8];
-  if (kFold) {
-    if (col_ok) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
-    }
-  } else if (col_ok) {
-    load8f(static_cast<const T*>(ep.bias) + n, b8);
-  }
   T* out = static_cast<T*>(ep.out);
 #pragma unroll
   for (int pass = 0; pass < NPASS; ++pass) {
@@ -205,8 +214,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       float xv[8], pv[8];
       frag_to_f32(px[pass], xv);
       if (EPI == kEpiProj) {
-        float g8[8], u[8];
-        load8f(static_cast<const T*>(ep.gamma) + n, g8);
+        float u[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pv[e] = round_t<T>(v[e] + b8[e]);   // attention branch p, as stored
@@ -266,8 +274,8 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
                                                      int K, int splits, GemmEpiArgs ep) {
   constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
   constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
-  // pipeline stages, or the staged fp32 tile plus one float2 per tile row
-  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + G::BM * 8;
+  // pipeline stages, or the staged fp32 tile plus one float2 per tile row and column
+  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + (G::BM + G::BN) * 8;
   constexpr int SMEM = 2 * STAGE > EBYTES ? 2 * STAGE : EBYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 // tile epilogue as the direct path.
 template <typename T, int EPI, class G>
 __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int splits, GemmEpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + G::BM * 8];
+  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + (G::BM + G::BN) * 8];
   constexpr int NPASS = G::BM / 16;
   const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
   const int t = xcd_contiguous(blockIdx.x, nM * nN);
