@@ -29,6 +29,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# Per-source additions.  Attention: matrix-core results in ordinary VGPRs -- the kernel
+# works on its score and output accumulators with VALU ops every key tile, and
+# accumulator-register results cost a copy each way (112 moves per tile).  The GEMMs keep
+# the default (measured slower with it).
+SOURCE_FLAGS = {"rs_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = [
     "-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
     "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include"),
@@ -52,7 +57,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc] + HIP_FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

@@ -105,8 +105,12 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
       const int key = min(kt * 64 + r, L - 1);
       load_frag(rk[i], kbase + (size_t)key * ldqk);
       load_frag(rv[i], vbase + (size_t)r * Lp + kt * 64);
+    }
+    if (kt * 64 + 64 > L) {  // the last, ragged key tile (uniform test)
       const int nv = L - (kt * 64 + lc * 8);
-      if (nv < 8) mask_tail(rv[i], nv < 0 ? 0 : nv);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (nv < 8) mask_tail(rv[i], nv < 0 ? 0 : nv);
     }
   };
   auto sstore = [&](int buf) {
@@ -127,6 +131,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   float m_run = -INFINITY, l_run = 0.f;
   const int nk = (L + 63) / 64;
 
+  // A wave whose 16 queries all lie past the sequence end (in the last query block of a
+  // ragged L) only helps stage K/V and meets the barriers.
+  const bool active = q0 < L;
   gload(0);
   sstore(0);
   __syncthreads();
@@ -135,66 +142,67 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     if (more) gload(kt + 1);
     const char* Ks = smem + (kt & 1) * 2 * TB;
     const char* Vs = Ks + TB;
-
-    // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
-    f32x4 s[4];
+    if (active) {
+      // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
+      f32x4 s[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = j * 16 + l16;
+      for (int j = 0; j < 4; ++j) {
+        s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = j * 16 + l16;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c = ks * 4 + g;
-        Frag8<T> kf;
-        load_frag(kf, Ks + r * ROWB + c * CB);
-        s[j] = mma16(s[j], kf, qf[ks]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = ks * 4 + g;
+          Frag8<T> kf;
+          load_frag(kf, Ks + r * ROWB + c * CB);
+          s[j] = mma16(s[j], kf, qf[ks]);
+        }
       }
-    }
-    if (kt * 64 + 64 > L) {
+      if (kt * 64 + 64 > L) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (kt * 64 + j * 16 + 4 * g + v >= L) s[j][v] = -INFINITY;
+      }
+      float mx = s[0][0];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (kt * 64 + j * 16 + 4 * g + v >= L) s[j][v] = -INFINITY;
-    }
-    float mx = s[0][0];
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      const float mb = m_new * scale_log2;
+      float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    const float mb = m_new * scale_log2;
-    float psum = 0.f;
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], scale_log2, -mb));
+          s[j][v] = p;
+          psum += p;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], scale_log2, -mb));
-        s[j][v] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+      for (int d = 0; d < 4; ++d) o[d] *= alpha;
 
-    Frag8<T> pf[2];
-    pack_p(pf[0], s[0], s[1]);
-    pack_p(pf[1], s[2], s[3]);
+      Frag8<T> pf[2];
+      pack_p(pf[0], s[0], s[1]);
+      pack_p(pf[1], s[2], s[3]);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int r = d * 16 + l16;
-      const char* vrow = Vs + r * ROWB;
+      for (int d = 0; d < 4; ++d) {
+        const int r = d * 16 + l16;
+        const char* vrow = Vs + r * ROWB;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int ca = 4 * kc + (g >> 1), cb = ca + 2;
-        const int half = (g & 1) * (CB / 2);
-        Frag8<T> vf;
-        load_vt(vf, vrow + ca * CB + half, vrow + cb * CB + half);
-        o[d] = mma16(o[d], vf, pf[kc]);
+        for (int kc = 0; kc < 2; ++kc) {
+          const int ca = 4 * kc + (g >> 1), cb = ca + 2;
+          const int half = (g & 1) * (CB / 2);
+          Frag8<T> vf;
+          load_vt(vf, vrow + ca * CB + half, vrow + cb * CB + half);
+          o[d] = mma16(o[d], vf, pf[kc]);
+        }
       }
     }
     if (more) sstore((kt + 1) & 1);
