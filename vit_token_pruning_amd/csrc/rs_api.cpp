@@ -141,7 +141,7 @@ rs_status check_schedule(int depth, int L, const int* prune, const double* ratio
 
 // ------------------------------------------------------------------ workspace
 struct BlockWs {
-  void *qk, *vt, *o, *p, *xp, *h, *xhat;
+  void *qkv, *o, *p, *xp, *h, *xhat;
   float* part;    // score partials of x_hat rows
   float* st_x;    // slice partials of the block input rows (LayerNorm 1)
   float* st_xp;   // slice partials of x' rows (LayerNorm 2)
@@ -166,9 +166,8 @@ size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
 size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws) {
   const size_t e = esize(d.dtype), M = (size_t)B * L, C = d.C;
   const size_t st = M * rs::stat_stride(d.C) * 8;
-  const size_t sizes[12] = {
-      M * 2 * C * e,                                     // qk: Q | K
-      (size_t)B * d.heads * 64 * rs::padded_len(L) * e,  // vt: V^T per head
+  const size_t sizes[11] = {
+      M * 3 * C * e,                                     // qkv: Q | K | V
       M * C * e,                                         // o: attention output
       M * C * e,                                         // p: attention branch (proj out)
       M * C * e,                                         // xp: x' * gamma2 (fc1 input)
@@ -178,14 +177,14 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
       st, st, st,                                        // slice partials
       rs::kSplitWsBytes,                                 // split-K partial tiles
   };
-  void* p[12];
-  const size_t off = carve_seq(base, sizes, 12, p);
+  void* p[11];
+  const size_t off = carve_seq(base, sizes, 11, p);
   if (ws) {
-    ws->qk = p[0]; ws->vt = p[1]; ws->o = p[2]; ws->p = p[3]; ws->xp = p[4]; ws->h = p[5];
-    ws->xhat = p[6]; ws->part = static_cast<float*>(p[7]);
-    ws->st_x = static_cast<float*>(p[8]); ws->st_xp = static_cast<float*>(p[9]);
-    ws->st_xhat = static_cast<float*>(p[10]);
-    ws->split = static_cast<float*>(p[11]);
+    ws->qkv = p[0]; ws->o = p[1]; ws->p = p[2]; ws->xp = p[3]; ws->h = p[4];
+    ws->xhat = p[5]; ws->part = static_cast<float*>(p[6]);
+    ws->st_x = static_cast<float*>(p[7]); ws->st_xp = static_cast<float*>(p[8]);
+    ws->st_xhat = static_cast<float*>(p[9]);
+    ws->split = static_cast<float*>(p[10]);
   }
   return off;
 }
@@ -285,8 +284,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
   const double Md = M, Cd = C;
   {
     rs::GemmEpiArgs ep;
-    ep.out = ws.qk; ep.ldo = 2 * C;
-    ep.vt = ws.vt; ep.vcol0 = 2 * C; ep.L = L; ep.Lp = rs::padded_len(L); ep.heads = d.heads;
+    ep.out = ws.qkv; ep.ldo = 3 * C;
     ep.stats_in = st_x; ep.fold_c = fw.cq; ep.fold_d = fw.dq; ep.eps = d.ln_eps; ep.C = C;
     ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_QKV, 2.0 * Md * 3 * Cd * Cd, st, [&] {
@@ -294,7 +292,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     }));
   }
   RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
-    return rs::launch_attention(dt, ws.qk, ws.vt, ws.o, B, L, d.heads, rs::padded_len(L), st);
+    return rs::launch_attention(dt, ws.qkv, ws.o, B, L, d.heads, st);
   }));
   {
     rs::GemmEpiArgs ep;

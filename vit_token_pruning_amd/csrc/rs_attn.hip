@@ -12,10 +12,15 @@
 //    work inside a tile beyond the 4 lane groups, the rescale factor applies to the
 //    lane's own output registers, and the probabilities are already in the register
 //    layout the P V product wants as its B operand (no LDS round trip for P).
-//  - K tiles [64 keys][64 d] and V^T tiles [64 d][64 keys] are staged in LDS, double
-//    buffered, each row padded by 16 bytes so the 16 rows of a fragment read fall on
-//    distinct banks; V^T comes pre-transposed from the QKV epilogue, so both products
-//    read K-contiguous fragments.
+//  - K and V tiles [64 keys][64 d] are staged in LDS row-major, straight from the QKV
+//    output rows, double buffered; K rows padded by 16 bytes so the 16 rows of a K
+//    fragment read fall on distinct banks, V rows by 32 bytes so the 8 rows x 32 bytes of
+//    one half-wave transpose read do.  Keys past the sequence end are clamped to the
+//    last row: finite values that meet probability 0.
+//  - the V^T fragments of the P V product come from the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16): within each 16-lane group, lane j names 4 consecutive d of
+//    key row base + j/4 and receives d0 + j of the 4 keys base .. base + 3.  fp32 reads
+//    the 8 keys of a fragment one element at a time.
 //  - exp2 with log2(e)/sqrt(d) folded into one FMA per score; the hardware exp2 is used
 //    directly (results below 2^-126 flush to zero, which a softmax over at least one
 //    term equal to 1 cannot notice).
@@ -24,15 +29,6 @@
 
 namespace rs {
 namespace {
-
-template <typename T>
-__device__ __forceinline__ void mask_tail(Frag8<T>& f, int nvalid) {
-  // zero elements nvalid..7 of the fragment (keys past the sequence end)
-  T* e = reinterpret_cast<T*>(&f);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i >= nvalid) e[i] = from_f32<T>(0.f);
-}
 
 // The 8 k-slots of P^T for lane group g and 32-key chunk kc hold keys
 // {32kc + 4g + v} (slots 0..3, from score tile 2kc) and {32kc + 16 + 4g + v} (slots 4..7,
@@ -47,14 +43,32 @@ __device__ __forceinline__ void pack_p(Frag8<float>& f, const f32x4& a, const f3
   f.v[0] = __builtin_bit_cast(u32x4, a);
   f.v[1] = __builtin_bit_cast(u32x4, b);
 }
-__device__ __forceinline__ void load_vt(Frag8<bf16>& f, const char* lo, const char* hi) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(lo);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(hi);
-  f.v = u32x4{a[0], a[1], b[0], b[1]};
+// V^T fragment for d = d0 + l16 and the keys of lane group g in 32-key chunk kc (the
+// slot assignment of pack_p): keys kb + 0..3 (slots 0-3) and kb + 16 .. kb + 19 (slots
+// 4-7), kb = 32 kc + 4 g.  Vs rows are keys, ROWBV bytes apart.
+template <int ROWBV>
+__device__ __forceinline__ void load_vt(Frag8<bf16>& f, const char* Vs, int kb, int d0, int l16) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const char* pa = Vs + (kb + (l16 >> 2)) * ROWBV + (d0 + 4 * (l16 & 3)) * 2;
+#if __HIP_DEVICE_COMPILE__
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pa));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pa + 16 * ROWBV));
+#else
+  const v4i16 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+#endif
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
-__device__ __forceinline__ void load_vt(Frag8<float>& f, const char* lo, const char* hi) {
-  f.v[0] = *reinterpret_cast<const u32x4*>(lo);
-  f.v[1] = *reinterpret_cast<const u32x4*>(hi);
+template <int ROWBV>
+__device__ __forceinline__ void load_vt(Frag8<float>& f, const char* Vs, int kb, int d0, int l16) {
+  float* e = reinterpret_cast<float*>(&f);
+  const char* col = Vs + (d0 + l16) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e[i] = *reinterpret_cast<const float*>(col + (kb + i) * ROWBV);
+    e[4 + i] = *reinterpret_cast<const float*>(col + (kb + 16 + i) * ROWBV);
+  }
 }
 __device__ __forceinline__ void store_o4(bf16* p, const f32x4& o, float s) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0] * s, o[1] * s), pack_bf16x2(o[2] * s, o[3] * s)};
@@ -64,16 +78,16 @@ __device__ __forceinline__ void store_o4(float* p, const f32x4& o, float s) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk,
-                                                        const T* __restrict__ vt,
-                                                        T* __restrict__ out, int L, int H, int Lp,
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv,
+                                                        T* __restrict__ out, int L, int H,
                                                         float scale_log2) {
   constexpr int CB = Chunk<T>::bytes;  // 8 elements
-  constexpr int ROWB = 8 * CB + 16;    // 64 elements + 16 bytes of padding
-  constexpr int TB = 64 * ROWB;        // one 64 x 64 tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB];
+  constexpr int ROWB = 8 * CB + 16;    // K rows: 64 elements + 16 bytes of padding
+  constexpr int ROWBV = 8 * CB + 32;   // V rows: 64 elements + 32 bytes of padding
+  constexpr int TBK = 64 * ROWB, TB = TBK + 64 * ROWBV;  // one K tile + one V tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * TB];
 
-  const int C = H * 64, ldqk = 2 * C;
+  const int C = H * 64, ldqkv = 3 * C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   // launch index -> (query block, head, sample), query blocks fastest; each XCD gets a
@@ -88,40 +102,32 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   Frag8<T> qf[2];
   {
     const int q = min(q0 + l16, L - 1);
-    const T* qp = qk + (row0 + q) * ldqk + h * 64 + g * 8;
+    const T* qp = qkv + (row0 + q) * ldqkv + h * 64 + g * 8;
     load_frag(qf[0], qp);
     load_frag(qf[1], qp + 32);
   }
 
-  // staging: 2 chunks of K rows and 2 chunks of V^T rows per thread per tile
+  // staging: 2 chunks of K rows and 2 chunks of V rows per thread per tile
   const int lc = tid & 7, lr = tid >> 3;
-  const T* kbase = qk + row0 * ldqk + C + h * 64 + lc * 8;
-  const T* vbase = vt + (size_t)(b * H + h) * 64 * Lp + lc * 8;
+  const T* kbase = qkv + row0 * ldqkv + C + h * 64 + lc * 8;
+  const T* vbase = kbase + C;
   Frag8<T> rk[2], rv[2];
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = lr + 32 * i;
-      const int key = min(kt * 64 + r, L - 1);
-      load_frag(rk[i], kbase + (size_t)key * ldqk);
-      load_frag(rv[i], vbase + (size_t)r * Lp + kt * 64);
-    }
-    if (kt * 64 + 64 > L) {  // the last, ragged key tile (uniform test)
-      const int nv = L - (kt * 64 + lc * 8);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (nv < 8) mask_tail(rv[i], nv < 0 ? 0 : nv);
+      const int key = min(kt * 64 + lr + 32 * i, L - 1);
+      load_frag(rk[i], kbase + (size_t)key * ldqkv);
+      load_frag(rv[i], vbase + (size_t)key * ldqkv);
     }
   };
   auto sstore = [&](int buf) {
-    char* Ks = smem + buf * 2 * TB;
-    char* Vs = Ks + TB;
+    char* Ks = smem + buf * TB;
+    char* Vs = Ks + TBK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = lr + 32 * i;
-      const int off = r * ROWB + lc * CB;
-      store_frag(Ks + off, rk[i]);
-      store_frag(Vs + off, rv[i]);
+      store_frag(Ks + r * ROWB + lc * CB, rk[i]);
+      store_frag(Vs + r * ROWBV + lc * CB, rv[i]);
     }
   };
 
@@ -140,8 +146,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     if (more) gload(kt + 1);
-    const char* Ks = smem + (kt & 1) * 2 * TB;
-    const char* Vs = Ks + TB;
+    const char* Ks = smem + (kt & 1) * TB;
+    const char* Vs = Ks + TBK;
     if (active) {
       // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
       f32x4 s[4];
@@ -193,14 +199,10 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
       pack_p(pf[1], s[2], s[3]);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int r = d * 16 + l16;
-        const char* vrow = Vs + r * ROWB;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const int ca = 4 * kc + (g >> 1), cb = ca + 2;
-          const int half = (g & 1) * (CB / 2);
           Frag8<T> vf;
-          load_vt(vf, vrow + ca * CB + half, vrow + cb * CB + half);
+          load_vt<ROWBV>(vf, Vs, 32 * kc + 4 * g, d * 16, l16);
           o[d] = mma16(o[d], vf, pf[kc]);
         }
       }
@@ -222,18 +224,16 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 
 }  // namespace
 
-hipError_t launch_attention(Dtype dt, const void* qk, const void* vt, void* out, int B, int L,
-                            int H, int Lp, hipStream_t stream) {
+hipError_t launch_attention(Dtype dt, const void* qkv, void* out, int B, int L, int H,
+                            hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
   const int grid = ((L + 63) / 64) * H * B;
   if (dt == kBF16)
-    attention_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(qk),
-                                                     static_cast<const bf16*>(vt),
-                                                     static_cast<bf16*>(out), L, H, Lp, scale_log2);
+    attention_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(qkv),
+                                                     static_cast<bf16*>(out), L, H, scale_log2);
   else
-    attention_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(qk),
-                                                      static_cast<const float*>(vt),
-                                                      static_cast<float*>(out), L, H, Lp, scale_log2);
+    attention_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(qkv),
+                                                      static_cast<float*>(out), L, H, scale_log2);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Tile GEMM Y = A W^T on the gfx950 matrix cores with the block's fused epilogues:
-// QKV (LayerNorm 1 folded in, per-head transposed V), attention projection (bias,
+// QKV (LayerNorm 1 folded in), attention projection (bias,
 // x' = x + p, LayerNorm 2 statistics), fc1 (LayerNorm 2 folded in, GELU) and fc2 (bias,
 // residual re-formed in fp32, the per-token partial sums of squares of the MLP-sublayer
 // representation shift, and the next block's LayerNorm 1 statistics).
@@ -30,9 +30,8 @@
 //
 // Orientation: the weight fragment is the MFMA A operand and the activation fragment
 // the B operand, so a lane ends up holding 4 consecutive output columns of one row.
-// The epilogue stages the fp32 tile in LDS -- row-major for the row-wise epilogues
-// (bias, GELU, residual, score), transposed for the V columns of the QKV projection,
-// whose output is V^T per head -- so every global access is a row-contiguous line.
+// The epilogue stages the fp32 tile in LDS, row-major, so every global access is a
+// row-contiguous line of 8 elements per lane.
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
 
@@ -74,9 +73,8 @@ struct Tile {
 };
 
 // The epilogue of one 128 x 128 output tile, shared by the direct path and the split-K
-// reduction.  `stage(Cs, vtile)` writes the tile's fp32 accumulators to LDS -- Cs[m][n]
-// for the row-wise epilogues, Cs[n][m] for the V columns of QKV -- with every LDS byte
-// free when it is called.
+// reduction.  `stage(Cs)` writes the tile's fp32 accumulators to LDS as Cs[m][n], with
+// every LDS byte free when it is called.
 template <typename T, int EPI, class G, class Stage>
 __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep, int M, int N,
                                               int m0, int n0, int nt, Stage&& stage) {
@@ -89,7 +87,6 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   const int n = n0 + ec;
   const bool col_ok = n < N;
   const int nsl = stat_slices(ep.C), sstride = stat_stride(ep.C);
-  const bool vtile = EPI == kEpiQKV && n0 >= ep.vcol0;         // uniform per workgroup
 
   // Epilogue inputs from global memory (row statistics, x, p) for all of this thread's
   // rows are requested before the tile is staged, so their latency overlaps the staging
@@ -116,13 +113,9 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       }
     }
   }
-  // per-column constants of this thread's 8 columns (row pass), or of the tile's 128
-  // columns for the V pass (one per thread, handed over through LDS)
+  // per-column constants of this thread's 8 columns
   float b8[8], g8[8], c8[8], d8[8];
-  float2 cdv = make_float2(0.f, 0.f);
-  if (vtile) {
-    if (tid < G::BN && n0 + tid < N) cdv = make_float2(ep.fold_c[n0 + tid], ep.fold_d[n0 + tid]);
-  } else if (col_ok) {
+  if (col_ok) {
     if (kFold) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
@@ -133,12 +126,11 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   }
 
   float* Cs = reinterpret_cast<float*>(smem);
-  stage(Cs, vtile);
+  stage(Cs);
 
   // folded LayerNorm: each tile row's (mean * rstd, rstd), merged once from its slice
   // partials (equal-count merge) and shared through LDS
   float2* Rs = reinterpret_cast<float2*>(smem + G::BM * kCS * 4);
-  float2* CD = Rs + G::BM;   // V pass: (c, d) of each tile column
   if (kFold && tid < G::BM) {
     float mean = 0.f;
 #pragma unroll
@@ -154,30 +146,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     const float rstd = 1.0f / sqrtf(m2 / (float)ep.C + ep.eps);
     Rs[tid] = make_float2(mean * rstd, rstd);
   }
-  if (vtile && tid < G::BN) CD[tid] = cdv;
   __syncthreads();
-
-  if (vtile) {
-    // V^T [b][h][d][token]: a wave writes 64 consecutive tokens of one channel per store
-    T* vt = static_cast<T*>(ep.vt);
-    const int mm = tid & 127, half = tid >> 7;
-    const int m = m0 + mm;
-    if (m < M) {
-      const float mr = Rs[mm].x, rstd = Rs[mm].y;
-      const int bb = m / ep.L, tk = m - bb * ep.L;
-      T* vrow = vt + (size_t)bb * ep.heads * 64 * ep.Lp + tk;
-#pragma unroll 8
-      for (int jj = 0; jj < 64; ++jj) {
-        const int nn = half * 64 + jj, nc = n0 + nn;
-        if (nc < N) {
-          const float2 cd = CD[nn];
-          const float v = fmaf(rstd, Cs[nn * kCS + mm], fmaf(-mr, cd.x, cd.y));
-          vrow[(size_t)(nc - ep.vcol0) * ep.Lp] = from_f32<T>(v);
-        }
-      }
-    }
-    return;
-  }
 
   // row pass: 8 consecutive columns per thread; lanes 0-7 / 8-15 of a row cover its two
   // 64-column slices of this tile
@@ -274,8 +243,8 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
                                                      int K, int splits, GemmEpiArgs ep) {
   constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
   constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
-  // pipeline stages, or the staged fp32 tile plus one float2 per tile row and column
-  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + (G::BM + G::BN) * 8;
+  // pipeline stages, or the staged fp32 tile plus one float2 per tile row
+  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + G::BM * 8;
   constexpr int SMEM = 2 * STAGE > EBYTES ? 2 * STAGE : EBYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -431,25 +400,14 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
       }
     return;
   }
-  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, bool vtile) {
-    if (vtile) {
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) Cs[(n + v) * kCS + m] = acc[j][i][v];
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
-          *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
-        }
-    }
+      for (int i = 0; i < TM; ++i) {
+        const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
+        *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
+      }
   });
 }
 
@@ -458,13 +416,13 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 // tile epilogue as the direct path.
 template <typename T, int EPI, class G>
 __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int splits, GemmEpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + (G::BM + G::BN) * 8];
+  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + G::BM * 8];
   constexpr int NPASS = G::BM / 16;
   const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
   const int t = xcd_contiguous(blockIdx.x, nM * nN);
   const int mt = t / nN, nt = t - mt * nN;
   const int m0 = mt * G::BM, n0 = nt * G::BN;
-  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, bool vtile) {
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs) {
     const int tid = threadIdx.x, er = tid >> 4, ec = (tid & 15) * 8;
     // Rows and columns past the matrix edge read a clamped, written element instead of
     // branching, so a split's 16 loads per thread are all in flight together; the
@@ -495,16 +453,8 @@ __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int 
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
       const int mm = pass * 16 + er;
-      if (vtile) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Cs[(ec + e) * kCS + mm] = a[pass][0][e];
-          Cs[(ec + 4 + e) * kCS + mm] = a[pass][1][e];
-        }
-      } else {
-        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec) = a[pass][0];
-        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec + 4) = a[pass][1];
-      }
+      *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec) = a[pass][0];
+      *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec + 4) = a[pass][1];
     }
   });
 }

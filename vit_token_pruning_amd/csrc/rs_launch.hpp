@@ -15,8 +15,6 @@ constexpr int kGemmTile = 128;
 // Score partials per token written by the fc2 epilogue: one per 64-column wave slice
 // of each 128-column tile.
 inline int score_parts(int C) { return 2 * ((C + kGemmTile - 1) / kGemmTile); }
-// Padded key length of the transposed V buffer (whole 64-key tiles).
-inline int padded_len(int L) { return (L + 63) / 64 * 64; }
 
 // LayerNorm is folded into the GEMM that consumes it:
 //   LN(z) W^T + b = rstd * (z W'^T - mu * c) + d,  W' = W diag(gamma), c = W' 1, d = W beta + b
@@ -27,7 +25,7 @@ __host__ __device__ inline int stat_slices(int C) { return C / 64; }
 __host__ __device__ inline int stat_stride(int C) { return (C / 64 + 1) / 2 * 2; }  // float2 per row
 
 enum GemmEpilogue {
-  kEpiQKV = 0,   // LN1 folded; Q|K -> qk [M][2C]; V -> vt [B][H][64][Lp] (transposed per head)
+  kEpiQKV = 0,   // LN1 folded; Q|K|V -> qkv [M][3C]
   kEpiProj = 1,  // p = acc + b -> out; x' = x + p -> out2; LN2 slice partials of x' -> stats_out
   kEpiGelu = 2,  // LN2 folded, GELU -> out [M][N]                 (fc1)
   kEpiFc2 = 3    // y = acc + b2; out = (x + p) + y; score partials; LN1 slice partials of out
@@ -37,9 +35,6 @@ struct GemmEpiArgs {
   const void* bias = nullptr;  // [N]
   void* out = nullptr;         // row stride ldo
   int ldo = 0;
-  // kEpiQKV: output columns >= vcol0 (= 2C, a multiple of the tile width) are V
-  void* vt = nullptr;
-  int vcol0 = 0, L = 1, Lp = 64, heads = 1;
   // kEpiProj / kEpiFc2: x' = x + p is re-formed in fp32 from the block input and the
   // attention branch
   const void* x = nullptr;
@@ -116,9 +111,9 @@ constexpr int kMaxFoldJobs = 8;
 hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStream_t stream);
 
 // Fused attention, one (sample, head, 64-query block) per workgroup.
-// qk [B*L][2C] (Q at columns h*64.., K at C + h*64..), vt [B][H][64][Lp] -> out [B*L][C].
-hipError_t launch_attention(Dtype dt, const void* qk, const void* vt, void* out, int B, int L,
-                            int H, int Lp, hipStream_t stream);
+// qkv [B*L][3C] (Q at columns h*64.., K at C + h*64.., V at 2C + h*64..) -> out [B*L][C].
+hipError_t launch_attention(Dtype dt, const void* qkv, void* out, int B, int L, int H,
+                            hipStream_t stream);
 
 // scores[r] = || fx[r] - x[r] ||_2 over C.
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
