@@ -13,10 +13,12 @@
 //    lane's own output registers, and the probabilities are already in the register
 //    layout the P V product wants as its B operand (no LDS round trip for P).
 //  - K and V tiles [64 keys][64 d] are staged in LDS row-major, straight from the QKV
-//    output rows, double buffered; K rows padded by 16 bytes so the 16 rows of a K
-//    fragment read fall on distinct banks, V rows by 32 bytes so the 8 rows x 32 bytes of
-//    one half-wave transpose read do.  Keys past the sequence end are clamped to the
-//    last row: finite values that meet probability 0.
+//    output rows, double buffered.  bf16: global -> LDS directly (16 bytes per lane, a
+//    wave fills 8 whole 128-byte rows), one tile ahead of the math, with 16-byte chunk c
+//    of row r at slot c ^ (r % 8) so the K fragment reads (16 rows, one chunk) and the
+//    V transpose reads (8 rows x 32 bytes per half-wave) fall on distinct banks.  fp32
+//    is staged through registers into padded rows.  Keys past the sequence end are
+//    clamped to the last row: finite values that meet probability 0.
 //  - the V^T fragments of the P V product come from the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16): within each 16-lane group, lane j names 4 consecutive d of
 //    key row base + j/4 and receives d0 + j of the 4 keys base .. base + 3.  fp32 reads
@@ -45,23 +47,29 @@ __device__ __forceinline__ void pack_p(Frag8<float>& f, const f32x4& a, const f3
 }
 // V^T fragment for d = d0 + l16 and the keys of lane group g in 32-key chunk kc (the
 // slot assignment of pack_p): keys kb + 0..3 (slots 0-3) and kb + 16 .. kb + 19 (slots
-// 4-7), kb = 32 kc + 4 g.  Vs rows are keys, ROWBV bytes apart.
-template <int ROWBV>
+// 4-7), kb = 32 kc + 4 g.  bf16 V rows are 128 bytes with swizzled 16-byte chunks.
+__device__ __forceinline__ const char* vt_addr(const char* Vs, int row, int d) {
+  const int c = d >> 3;                          // 16-byte chunk of element d
+  return Vs + row * 128 + ((c ^ (row & 7)) << 4) + ((d & 7) << 1);
+}
 __device__ __forceinline__ void load_vt(Frag8<bf16>& f, const char* Vs, int kb, int d0, int l16) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const char* pa = Vs + (kb + (l16 >> 2)) * ROWBV + (d0 + 4 * (l16 & 3)) * 2;
+  const int row = kb + (l16 >> 2), d = d0 + 4 * (l16 & 3);
+  const char* pa = vt_addr(Vs, row, d);
+  const char* pb = vt_addr(Vs, row + 16, d);
 #if __HIP_DEVICE_COMPILE__
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pa));
-  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pa + 16 * ROWBV));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb));
 #else
   const v4i16 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
 #endif
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
+// fp32: padded rows of ROWBV bytes, no swizzle
 template <int ROWBV>
-__device__ __forceinline__ void load_vt(Frag8<float>& f, const char* Vs, int kb, int d0, int l16) {
+__device__ __forceinline__ void load_vt_f32(Frag8<float>& f, const char* Vs, int kb, int d0, int l16) {
   float* e = reinterpret_cast<float*>(&f);
   const char* col = Vs + (d0 + l16) * 4;
 #pragma unroll
@@ -81,11 +89,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv,
                                                         T* __restrict__ out, int L, int H,
                                                         float scale_log2) {
-  constexpr int CB = Chunk<T>::bytes;  // 8 elements
-  constexpr int ROWB = 8 * CB + 16;    // K rows: 64 elements + 16 bytes of padding
-  constexpr int ROWBV = 8 * CB + 32;   // V rows: 64 elements + 32 bytes of padding
-  constexpr int TBK = 64 * ROWB, TB = TBK + 64 * ROWBV;  // one K tile + one V tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * TB];
+  constexpr bool kDirect = sizeof(T) == 2;
+  constexpr int CB = Chunk<T>::bytes;                  // 8 elements
+  constexpr int ROWB = kDirect ? 128 : 8 * CB + 16;    // K rows (fp32: 16 bytes of padding)
+  constexpr int ROWBV = kDirect ? 128 : 8 * CB + 32;   // V rows (fp32: 32 bytes of padding)
+  // K and V tiles of the two buffers live in separate LDS arrays: each access below names
+  // a fixed one, which lets the compiler see that the math on one buffer does not touch
+  // the direct loads in flight into the other (it would otherwise wait for them)
+  __shared__ __attribute__((aligned(1024))) char k0[64 * ROWB], k1[64 * ROWB];
+  __shared__ __attribute__((aligned(1024))) char v0[64 * ROWBV], v1[64 * ROWBV];
 
   const int C = H * 64, ldqkv = 3 * C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -107,9 +119,12 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     load_frag(qf[1], qp + 32);
   }
 
-  // staging: 2 chunks of K rows and 2 chunks of V rows per thread per tile
+  // staging: thread (lr = tid / 8, lc = tid % 8) moves 16-byte chunks of K and V rows
+  // lr and lr + 32.  bf16 direct: lane lc of a wave fills LDS slot lc of its row, so it
+  // fetches global chunk lc ^ (row % 8); the wave's 1 KiB is rows 8 wave .. + 7 (+ 32).
   const int lc = tid & 7, lr = tid >> 3;
-  const T* kbase = qkv + row0 * ldqkv + C + h * 64 + lc * 8;
+  const int gc = kDirect ? (lc ^ (lr & 7)) : lc;       // (lr + 32) % 8 == lr % 8
+  const T* kbase = qkv + row0 * ldqkv + C + h * 64 + gc * 8;
   const T* vbase = kbase + C;
   Frag8<T> rk[2], rv[2];
   auto gload = [&](int kt) {
@@ -120,15 +135,24 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
       load_frag(rv[i], vbase + (size_t)key * ldqkv);
     }
   };
-  auto sstore = [&](int buf) {
-    char* Ks = smem + buf * TB;
-    char* Vs = Ks + TBK;
+  auto sstore = [&](char* Ks, char* Vs) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = lr + 32 * i;
       store_frag(Ks + r * ROWB + lc * CB, rk[i]);
       store_frag(Vs + r * ROWBV + lc * CB, rv[i]);
     }
+  };
+  auto dload = [&](int kt, char* Ks, char* Vs) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(kt * 64 + lr + 32 * i, L - 1);
+      load_lds16(kbase + (size_t)key * ldqkv, Ks + (wave * 8 + 32 * i) * 128);
+      load_lds16(vbase + (size_t)key * ldqkv, Vs + (wave * 8 + 32 * i) * 128);
+    }
+  };
+  auto kaddr = [&](const char* Ks, int r, int c) {
+    return kDirect ? Ks + r * 128 + ((c ^ (r & 7)) << 4) : Ks + r * ROWB + c * CB;
   };
 
   f32x4 o[4];
@@ -140,75 +164,101 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   // A wave whose 16 queries all lie past the sequence end (in the last query block of a
   // ragged L) only helps stage K/V and meets the barriers.
   const bool active = q0 < L;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    const char* Ks = smem + (kt & 1) * TB;
-    const char* Vs = Ks + TBK;
-    if (active) {
-      // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
-      f32x4 s[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = j * 16 + l16;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c = ks * 4 + g;
-          Frag8<T> kf;
-          load_frag(kf, Ks + r * ROWB + c * CB);
-          s[j] = mma16(s[j], kf, qf[ks]);
-        }
-      }
-      if (kt * 64 + 64 > L) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (kt * 64 + j * 16 + 4 * g + v >= L) s[j][v] = -INFINITY;
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      const float mb = m_new * scale_log2;
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], scale_log2, -mb));
-          s[j][v] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o[d] *= alpha;
 
-      Frag8<T> pf[2];
-      pack_p(pf[0], s[0], s[1]);
-      pack_p(pf[1], s[2], s[3]);
+  // The math of one key tile from LDS buffers Ks, Vs.
+  auto tile = [&](int kt, const char* Ks, const char* Vs) {
+    // S^T tile: s[j] lane (g, l16) = keys 16j + 4g + v of query l16
+    f32x4 s[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+    for (int j = 0; j < 4; ++j) {
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = j * 16 + l16;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          Frag8<T> vf;
-          load_vt<ROWBV>(vf, Vs, 32 * kc + 4 * g, d * 16, l16);
-          o[d] = mma16(o[d], vf, pf[kc]);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag8<T> kf;
+        load_frag(kf, kaddr(Ks, r, ks * 4 + g));
+        s[j] = mma16(s[j], kf, qf[ks]);
       }
     }
-    if (more) sstore((kt + 1) & 1);
+    if (kt * 64 + 64 > L) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kt * 64 + j * 16 + 4 * g + v >= L) s[j][v] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    const float mb = m_new * scale_log2;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], scale_log2, -mb));
+        s[j][v] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+
+    Frag8<T> pf[2];
+    pack_p(pf[0], s[0], s[1]);
+    pack_p(pf[1], s[2], s[3]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        Frag8<T> vf;
+        if constexpr (kDirect) load_vt(vf, Vs, 32 * kc + 4 * g, d * 16, l16);
+        else load_vt_f32<ROWBV>(vf, Vs, 32 * kc + 4 * g, d * 16, l16);
+        o[d] = mma16(o[d], vf, pf[kc]);
+      }
+    }
+  };
+
+  if constexpr (kDirect) {
+    // the loads of tile kt + 1 go out right after the barrier that frees their buffer;
+    // two tiles per trip so that every access names its buffer statically
+    auto step = [&](int kt, char* kc, char* vc, char* kn, char* vn) {
+      wait_vmem<0>();          // this wave's part of tile kt (and Q) has landed
+      barrier_nofence();       // ... and every wave's; tile kt - 1's reads are done
+      if (kt + 1 < nk) dload(kt + 1, kn, vn);
+      if (active) tile(kt, kc, vc);
+    };
+    dload(0, k0, v0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, k0, v0, k1, v1);
+      step(kt + 1, k1, v1, k0, v0);
+    }
+    if (kt < nk) step(kt, k0, v0, k1, v1);
+  } else {
+    gload(0);
+    sstore(k0, v0);
     __syncthreads();
+    int kt = 0;
+    auto step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) {
+      const bool more = kt + 1 < nk;
+      if (more) gload(kt + 1);
+      if (active) tile(kt, kc, vc);
+      if (more) sstore(kn, vn);
+      __syncthreads();
+    };
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, k0, v0, k1, v1);
+      step(kt + 1, k1, v1, k0, v0);
+    }
+    if (kt < nk) step(kt, k0, v0, k1, v1);
   }
 
   float lt = l_run + __shfl_xor(l_run, 16, 64);
