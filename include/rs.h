@@ -114,7 +114,14 @@ rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C
  *  blocks   [depth] weight sets.
  *  out      [B][L_final][C] encoder output (L_final from rs_encoder_out_len).
  *  out_idx  [B][L_final] original token index of every output row.
- *  workspace/ws_bytes   >= rs_workspace_bytes(desc, depth, B, L). */
+ *  workspace/ws_bytes   >= rs_workspace_bytes(desc, depth, B, L).
+ * Concurrency: when B >= 2 and each half of the batch still has >= 1024 rows after the
+ * last pruning (ceil(B/2) * L_final and floor(B/2) * L_final), the batch runs as two
+ * lanes -- samples [0, ceil(B/2)) on `stream`, the rest on a stream the library owns
+ * (default priority), forked from and joined back into `stream` with events -- so one
+ * lane's memory-bound phases overlap the other's matrix work.  Per-sample results do not
+ * depend on the lane split except through a GEMM's split over K, which depends on its
+ * row count.  All work is ordered after prior work on `stream` and before later work. */
 rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* blocks,
                              int depth, const void* x, int B, int L,
                              const int* prune_layers, const double* keep_ratios, int n_prune,
@@ -130,6 +137,10 @@ rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers,
  * invalid description. */
 size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L);
 
+/* Host only: most lanes rs_encoder_forward may use (1 or 2; default 2).  1 keeps every
+ * launch on the caller's stream.  Process-wide; affects calls made after it returns. */
+rs_status rs_set_max_lanes(int lanes);
+
 /* Message for the calling thread's last failed call ("" if none); valid until the next
  * call on that thread. */
 const char* rs_last_error(void);
@@ -138,7 +149,8 @@ const char* rs_last_error(void);
  * Between rs_timing_begin(kernel) and rs_timing_end(), every launch of that kernel
  * class made by this library is bracketed by HIP events recorded on the stream it is
  * launched on.  rs_timing_end() waits for those events and returns the summed kernel
- * time, the number of launches and the summed algorithmic work of those launches
+ * time (launches of the two encoder lanes may overlap, and each then includes the time
+ * it shared the GPU), the number of launches and the summed algorithmic work of those launches
  * (flop for the GEMM and attention kernels, bytes for the memory-bound ones).
  * LayerNorm has no pass of its own: it is folded into the QKV and fc1 GEMMs, whose inputs'
  * row statistics come from the producing epilogue; RS_KERNEL_LN_PREP times the remaining

@@ -129,7 +129,7 @@ def test_encoder_validation(N):
     ws = lib.rs_workspace_bytes(ctypes.byref(d), 12, 4, 197)
     assert ws > 0
     st = lib.rs_encoder_forward(ctypes.byref(d), blocks, 12, FAKE, 4, 197, N.int_array([3, 6, 9]),
-                                N.dbl_array([0.7] * 3), 3, FAKE, FAKE, FAKE, ws - 256, None)
+                                N.dbl_array([0.7] * 3), 3, FAKE, FAKE, FAKE, ws // 4, None)
     assert st == N.RS_ERR_WORKSPACE
     blocks[5] = _weights(N, 0)
     st = lib.rs_encoder_forward(ctypes.byref(d), blocks, 12, FAKE, 4, 197, N.int_array([3, 6, 9]),
@@ -149,6 +149,14 @@ def test_workspace_query(N):
     fold = 3 * 384 * 384 * 2
     assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
     assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
+
+
+def test_set_max_lanes(N):
+    lib = N.lib()
+    assert lib.rs_set_max_lanes(0) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_set_max_lanes(3) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_set_max_lanes(1) == N.RS_OK
+    assert lib.rs_set_max_lanes(2) == N.RS_OK
 
 
 def test_timing_session_without_launches(N):

@@ -1,10 +1,13 @@
 """Full-size encoder parity (the four encoder workloads at their real batch and length,
 the launch configuration the benchmark times).
 
-rs_encoder_forward is checked bit-exactly against a chain of rs_block_forward calls at
+rs_encoder_forward is checked bit-exactly against chains of rs_block_forward calls at
 the same shapes (same kernels, deterministic), whose per-block results are checked
 against the oracle on sampled samples with teacher forcing: the oracle block is fed the
-GPU's own block input, so each comparison measures one block's rounding."""
+GPU's own block input, so each comparison measures one block's rounding.  The encoder
+runs a batch as two lanes (the first ceil(B/2) samples and the rest, on two streams)
+when each lane keeps >= 1024 rows after the last pruning; the reference chains run per
+lane, since a GEMM's split over K depends on its row count and so on the lane's batch."""
 import numpy as np
 import pytest
 
@@ -18,35 +21,33 @@ pytestmark = pytest.mark.gpu
 SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2]}
 
 
-@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l"])
-def test_encoder_full_size(name):
+def lanes(B, L_final):
+    if B < 2 or (B // 2) * L_final < 1024:
+        return [(0, B)]
+    return [(0, (B + 1) // 2), ((B + 1) // 2, B)]
+
+
+def chain_and_check(wl, blocks, wd, xd, samp):
+    """rs_block_forward chained over the encoder's schedule for the samples of xd, with
+    teacher-forced oracle checks of every block on the sample indices `samp` (local to
+    xd).  Returns the final rows, their original ids and the kept-set agreement count."""
     import torch
     import vit_token_pruning_amd as rs
-    wl = synth.WORKLOADS[name]
     spec = spec_of(wl)
-    x = synth.make_input(wl, 0)
-    blocks = synth.make_encoder_weights(wl, 0)
-    wd = [weights_to_dev(w, wl.dtype) for w in blocks]
-    xd = to_dev(x, wl.dtype)
-    lens, ks, L_final = O.schedule(wl.depth, wl.L, wl.prune_layers, wl.keep_ratios)
-
-    out, out_idx = rs.encoder_forward(spec, wd, xd, wl.prune_layers, wl.keep_ratios)
-    torch.cuda.synchronize()
-    assert tuple(out.shape) == (wl.B, L_final, wl.C)
-
-    samp = SAMPLED[name]
+    _, ks, _ = O.schedule(wl.depth, wl.L, wl.prune_layers, wl.keep_ratios)
     cur = xd
-    ids = np.tile(np.arange(wl.L), (wl.B, 1))
+    ids = np.tile(np.arange(wl.L), (xd.shape[0], 1))
     exact = total = 0
     for b in range(wl.depth):
         L = cur.shape[1]
         k = ks.get(b, L)
-        cur_host = to_host(cur[samp])
+        cur_host = to_host(cur[samp]) if samp else None
         r = rs.block_forward(spec, wd[b], cur, k)
         torch.cuda.synchronize()
-        y = to_host(r["y"][samp])
-        s = r["scores"][samp].cpu().numpy()
         kept_all = r["kept_idx"].cpu().numpy()
+        if samp:
+            y = to_host(r["y"][samp])
+            s = r["scores"][samp].cpu().numpy()
         for j, sb in enumerate(samp):
             ora = O.block_forward(cur_host[j], blocks[b], wl.heads, wl.ln_eps)
             check_block_output(y[j], ora["x_hat"], cur_host[j], wl.dtype)
@@ -58,6 +59,66 @@ def test_encoder_full_size(name):
             ids = np.take_along_axis(ids, kept_all.astype(np.int64), axis=1)
         cur = r["y_kept"]
     torch.cuda.synchronize()
-    assert torch.equal(out, cur), "encoder output differs from the chained blocks"
-    assert np.array_equal(out_idx.cpu().numpy(), ids)
-    print(f"{name}: exact kept-set agreement {exact}/{total} sampled prune stages")
+    return cur, ids, exact, total
+
+
+def check_encoder(wl, samples):
+    import torch
+    import vit_token_pruning_amd as rs
+    spec = spec_of(wl)
+    x = synth.make_input(wl, 0)
+    blocks = synth.make_encoder_weights(wl, 0)
+    wd = [weights_to_dev(w, wl.dtype) for w in blocks]
+    xd = to_dev(x, wl.dtype)
+    _, _, L_final = O.schedule(wl.depth, wl.L, wl.prune_layers, wl.keep_ratios)
+
+    out, out_idx = rs.encoder_forward(spec, wd, xd, wl.prune_layers, wl.keep_ratios)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (wl.B, L_final, wl.C)
+
+    exact = total = 0
+    for b0, b1 in lanes(wl.B, L_final):
+        samp = [s - b0 for s in samples if b0 <= s < b1]
+        cur, ids, e, t = chain_and_check(wl, blocks, wd, xd[b0:b1].contiguous(), samp)
+        exact, total = exact + e, total + t
+        assert torch.equal(out[b0:b1], cur), f"encoder lane {b0}:{b1} differs from the chained blocks"
+        assert np.array_equal(out_idx[b0:b1].cpu().numpy(), ids)
+    print(f"{wl.name} B{wl.B}: exact kept-set agreement {exact}/{total} sampled prune stages")
+
+
+@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l"])
+def test_encoder_full_size(name):
+    check_encoder(synth.WORKLOADS[name], SAMPLED[name])
+
+
+@pytest.mark.parametrize("B", [1, 3, 45])
+def test_encoder_one_lane_and_uneven_lanes(B):
+    """B = 1 and 3 run on the caller's stream alone (too few rows for two lanes); B = 45
+    (48 tokens left) splits into lanes of 23 and 22 samples."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["deit_s"], B=B, L=97, depth=4, prune_layers=(1, 2),
+                             keep_ratios=(0.7, 0.7))
+    check_encoder(wl, [B - 1])
+
+
+def test_encoder_lanes_setting():
+    """rs_set_max_lanes(1) runs the whole batch on the caller's stream; with two lanes the
+    results equal the per-lane chains (checked above), with one the full-batch chain."""
+    import torch
+    import vit_token_pruning_amd as rs
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["deit_s"], B=45, L=97, depth=3, prune_layers=(1,),
+                             keep_ratios=(0.7,))
+    spec = spec_of(wl)
+    blocks = synth.make_encoder_weights(wl, 0)
+    wd = [weights_to_dev(w, wl.dtype) for w in blocks]
+    xd = to_dev(synth.make_input(wl, 0), wl.dtype)
+    try:
+        rs.set_max_lanes(1)
+        out1, idx1 = rs.encoder_forward(spec, wd, xd, wl.prune_layers, wl.keep_ratios)
+        torch.cuda.synchronize()
+    finally:
+        rs.set_max_lanes(2)
+    cur, ids, _, _ = chain_and_check(wl, blocks, wd, xd, [])
+    assert torch.equal(out1, cur)
+    assert np.array_equal(idx1.cpu().numpy(), ids)

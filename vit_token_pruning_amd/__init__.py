@@ -15,7 +15,8 @@ from . import _native as N
 from ._native import BLOCK_FIELDS, KERNELS, RSError, lib  # noqa: F401
 
 __all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forward",
-           "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib"]
+           "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib",
+           "set_max_lanes"]
 
 _DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
 
@@ -178,6 +179,11 @@ def encoder_forward(spec: ModelSpec, blocks: List[Dict[str, torch.Tensor]], x: t
     enc = Encoder(spec, blocks, B, L, prune_layers, keep_ratios, device=x.device)
     out, idx = enc.forward(x)
     return out, idx
+
+
+def set_max_lanes(lanes: int) -> None:
+    """Most concurrent lanes (streams) the encoder may split a batch into: 1 or 2."""
+    N.check("rs_set_max_lanes", lib().rs_set_max_lanes(int(lanes)))
 
 
 class KernelTimer:
