@@ -89,7 +89,7 @@ def copy_probe(rs, torch):
 def summarize(dirs, workload):
     """Per-kernel averages of the counters in rocprofv3 result databases; HBM traffic of each
     kernel class from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by what the same
-    counters read for the 256 MiB copy probe (the gather dispatch with the largest grid)."""
+    counters read for the 2 GiB copy probe (the gather dispatch with the largest grid)."""
     import collections
     import glob
     import sqlite3
@@ -142,7 +142,7 @@ def kernel_sources_sha256():
     src = os.path.join(ROOT, "vit_token_pruning_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(src)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith((".hip", ".hpp", ".cpp")):
             h.update(open(os.path.join(src, f), "rb").read())
     return h.hexdigest()
 
@@ -169,6 +169,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="deit_s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the single-lane per-kernel breakdown and context pass, so every "
+                         "launch in the process is a timed-mode launch (for profiler runs)")
+    ap.add_argument("--kernel", default="fc1", choices=[k for k in ("ln_prep", "qkv", "attention",
+                    "proj", "fc1", "fc2_score", "topk", "gather")],
+                    help="roofline kernel when --no-breakdown is given")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB copy through the gather kernel (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -211,24 +217,27 @@ def main():
 
     # per-kernel breakdown (one step per kernel class, single lane so launches do not
     # overlap) to find the dominant kernel
-    per = {}
-    rs.set_max_lanes(1)
-    for kname in rs.KERNELS:
-        if kname == "score":
-            continue
-        with rs.KernelTimer(kname) as kt:
-            enc.forward(x)
-        per[kname] = {"ms": kt.total_ms, "launches": kt.launches, "work": kt.work}
-    dominant = max(per, key=lambda k: per[k]["ms"])
+    per, kt1 = {}, None
+    if args.no_breakdown:
+        dominant = args.kernel
+    else:
+        rs.set_max_lanes(1)
+        for kname in rs.KERNELS:
+            if kname == "score":
+                continue
+            with rs.KernelTimer(kname) as kt:
+                enc.forward(x)
+            per[kname] = {"ms": kt.total_ms, "launches": kt.launches, "work": kt.work}
+        dominant = max(per, key=lambda k: per[k]["ms"])
+        log("per-kernel ms/step (single lane):", {k: round(v["ms"], 4) for k, v in per.items()},
+            "dominant:", dominant)
+        # the dominant kernel alone on the GPU: its unshared rate, for context
+        with rs.KernelTimer(dominant) as kt1:
+            for _ in range(min(args.steps, 10)):
+                enc.forward(x)
+        rs.set_max_lanes(2)
+        torch.cuda.synchronize()
     bound = KERNEL_BOUND[dominant]
-    log("per-kernel ms/step (single lane):", {k: round(v["ms"], 4) for k, v in per.items()},
-        "dominant:", dominant)
-    # the dominant kernel alone on the GPU: its unshared rate, for context
-    with rs.KernelTimer(dominant) as kt1:
-        for _ in range(min(args.steps, 10)):
-            enc.forward(x)
-    rs.set_max_lanes(2)
-    torch.cuda.synchronize()
 
     # timed region: K steps of the encoder as it runs by default (two lanes when the batch
     # is large enough); the dominant kernel is event-timed on the stream each launch runs on
@@ -246,16 +255,18 @@ def main():
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step, {value:.1f} {wl.unit}/s")
 
     achieved = rate(kt.work, kt.total_ms)
-    achieved1 = rate(kt1.work, kt1.total_ms)
     roof = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK[bound],
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(achieved / PEAK[bound], 4),
             "traffic": stored_traffic(wl.name, dominant),
             "launches_per_step": kt.launches // args.steps,
             "avg_launch_us": round(kt.total_ms * 1e3 / max(1, kt.launches), 3),
-            # launches of the two encoder lanes overlap in the timed region; the same
-            # kernel with the batch on one stream (not timed for `value`):
-            "single_lane": {"achieved": round(achieved1, 2), "frac": round(achieved1 / PEAK[bound], 4),
-                            "avg_launch_us": round(kt1.total_ms * 1e3 / max(1, kt1.launches), 3)}}
+            }
+    if kt1 is not None:
+        # launches of the two encoder lanes overlap in the timed region; the same kernel
+        # with the batch on one stream (not timed for `value`):
+        achieved1 = rate(kt1.work, kt1.total_ms)
+        roof["single_lane"] = {"achieved": round(achieved1, 2), "frac": round(achieved1 / PEAK[bound], 4),
+                               "avg_launch_us": round(kt1.total_ms * 1e3 / max(1, kt1.launches), 3)}
 
     # algorithmic flop of one step under the schedule: 2 * (12 L C^2 + 2 L^2 C) per sample-block
     from_sched = 0.0
