@@ -162,6 +162,66 @@ def stored_traffic(workload, kernel):
     return None if v is None else float(v)
 
 
+def standalone(wl, steps):
+    """rs_score and rs_topk_gather alone at the workload's prune-stage shapes: algorithmic
+    bytes / kernel time against 8 TB/s.  Inputs rotate over >= 512 MiB of buffers (twice the
+    256 MB Infinity Cache) so every call reads from HBM.  Bytes per call: rs_score reads
+    f and x (2 M C e) and writes 4 M; rs_topk_gather reads 4 L scores and the k kept rows
+    (k C e) per sample and writes k C e + 4 k."""
+    import numpy as np
+    import torch
+    from vit_token_pruning_amd import _native as N
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    e = 2 if wl.dtype == "bf16" else 4
+    lib = N.lib()
+    code = N.RS_BF16 if wl.dtype == "bf16" else N.RS_F32
+    stream = torch.cuda.current_stream()
+    out = []
+    L = wl.L
+    for pl, r in zip(wl.prune_layers, wl.keep_ratios):
+        k = int(np.floor(r * L + 0.5))
+        B, C = wl.B, wl.C
+        M = B * L
+        nbuf = max(2, -(-(512 << 20) // (2 * M * C * e)))
+        g = torch.Generator(device="cuda").manual_seed(0)
+        fx = [torch.randn(B, L, C, device="cuda", generator=g).to(dt) for _ in range(nbuf)]
+        xs = [torch.randn(B, L, C, device="cuda", generator=g).to(dt) for _ in range(nbuf)]
+        sc = [torch.empty(B, L, device="cuda", dtype=torch.float32) for _ in range(nbuf)]
+        kept = torch.empty(B, k, device="cuda", dtype=torch.int32)
+        xk = torch.empty(B, k, C, device="cuda", dtype=dt)
+        hs = stream.cuda_stream
+
+        def score(i):
+            N.check("rs_score", lib.rs_score(fx[i].data_ptr(), xs[i].data_ptr(), B, L, C, code,
+                                             sc[i].data_ptr(), hs))
+
+        def select(i):
+            N.check("rs_topk_gather", lib.rs_topk_gather(sc[i].data_ptr(), xs[i].data_ptr(), B, L, C,
+                                                         code, k, wl.has_cls, kept.data_ptr(),
+                                                         xk.data_ptr(), hs))
+        for i in range(nbuf):
+            score(i)
+        torch.cuda.synchronize()
+        res = {"after_block": pl, "L": L, "k": k, "M": M, "buffers_MiB": round(nbuf * 2 * M * C * e / 2**20)}
+        for name, fn, nbytes in (("score", score, 2.0 * M * C * e + 4.0 * M),
+                                 ("topk_gather", select, B * (4.0 * L + 2.0 * k * C * e + 4.0 * k))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for it in range(steps):
+                fn(it % nbuf)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res[name] = {"us": round(us, 2), "bytes": int(nbytes), "GB_s": round(gbs, 1),
+                         "frac_hbm": round(gbs / PEAK["hbm"], 4)}
+        out.append(res)
+        del fx, xs, sc
+        torch.cuda.empty_cache()
+        L = k
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +229,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="deit_s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--standalone", action="store_true",
+                    help="time rs_score and rs_topk_gather alone at the prune-stage shapes "
+                         "(HBM-bound kernels, rotating >= 512 MiB of inputs); prints one JSON line")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the single-lane per-kernel breakdown and context pass, so every "
                          "launch in the process is a timed-mode launch (for profiler runs)")
@@ -198,6 +261,13 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.depth == 1:
         sys.exit("pick an encoder workload")
+    if args.standalone:
+        torch.cuda.set_device(0)
+        res = standalone(wl, args.steps)
+        print(json.dumps({"metric": "standalone rs_score / rs_topk_gather HBM throughput",
+                          "workload": wl.name, "unit": "GB/s", "peak": PEAK["hbm"], "stages": res}),
+              flush=True)
+        return
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     torch.cuda.set_device(0)
     x_np = synth.make_input(wl, 0)

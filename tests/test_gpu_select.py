@@ -58,6 +58,19 @@ def test_topk_gather_edges(B, L, k, cls, kind):
     _run(B, L, k, cls, kind, seed=L + 3 * k + B)
 
 
+# Batches of >= 32 samples copy the kept rows inside the top-k launch; L <= 256 takes the
+# rank path, longer L the radix select.  Row widths of 3 to 1032 16-byte units.
+FUSED = [(64, 1568, 784, False, 256), (40, 2000, 37, True, 64), (32, 1025, 1, True, 1024),
+         (33, 300, 299, False, 8), (32, 1024, 1024, True, 384), (48, 16384, 9000, False, 8),
+         (32, 256, 255, False, 8192), (36, 256, 1, True, 16), (32, 257, 128, True, 24),
+         (32, 40, 20, False, 8256)]
+
+
+@pytest.mark.parametrize("B,L,k,cls,C", FUSED)
+def test_topk_gather_fused_copy(B, L, k, cls, C):
+    _run(B, L, k, cls, "ties", seed=B + L + k, C=C)
+
+
 def test_topk_select_only_and_fp32_rows():
     import torch
     import vit_token_pruning_amd as rs

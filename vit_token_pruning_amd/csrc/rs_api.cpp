@@ -372,19 +372,38 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
   return RS_OK;
 }
 
+// Top-k of each sample and compaction of the kept rows of x (-> x_kept, nullable) and of
+// an optional second row set (x2 -> x2_kept, e.g. the rows' LayerNorm statistics).  Large
+// batches do it in one launch; small ones copy with a separate all-rows grid.
 rs_status run_select(int B, int L, int k, int has_cls, const float* scores, const float* part,
                      int P, float* scores_out, int32_t* kept, const int32_t* ids_in,
                      int32_t* ids_out, const void* x, void* x_kept, size_t row_bytes,
-                     hipStream_t st) {
+                     hipStream_t st, const void* x2 = nullptr, void* x2_kept = nullptr,
+                     size_t row_bytes2 = 0) {
   const double topk_bytes = (double)B * L * 4.0 * (part ? P : 1) + (scores_out ? B * L * 4.0 : 0.0) +
                             (double)B * k * 4.0 * (ids_out ? 2 : 1);
-  RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes, st, [&] {
-    return rs::launch_topk(scores, part, P, B, L, k, has_cls, scores_out, kept, ids_in, ids_out, st);
-  }));
+  rs::TopkCopy cp[2];
+  int nc = 0;
+  double copy_bytes = 0.0;
   if (x_kept) {
-    RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)row_bytes + B * k * 4.0, st, [&] {
-      return rs::launch_gather(x, kept, x_kept, B, L, k, (int)row_bytes, st);
-    }));
+    cp[nc++] = {x, x_kept, (int)row_bytes};
+    copy_bytes += 2.0 * B * k * (double)row_bytes;
+  }
+  if (x2_kept) {
+    cp[nc++] = {x2, x2_kept, (int)row_bytes2};
+    copy_bytes += 2.0 * B * k * (double)row_bytes2;
+  }
+  const bool fused = B >= rs::kTopkCopyMinBatch;
+  RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes + (fused ? copy_bytes : 0.0), st, [&] {
+    return rs::launch_topk(scores, part, P, B, L, k, has_cls, scores_out, kept, ids_in, ids_out,
+                           cp, fused ? nc : 0, st);
+  }));
+  if (!fused) {
+    for (int i = 0; i < nc; ++i) {
+      RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)cp[i].row_bytes + B * k * 4.0, st, [&] {
+        return rs::launch_gather(cp[i].src, kept, cp[i].dst, B, L, k, cp[i].row_bytes, st);
+      }));
+    }
   }
   return RS_OK;
 }
@@ -452,16 +471,12 @@ struct LaneRun {
     if ((s = run_block(*d, blocks[b], fw, cur, bw.st_x, B, curL, bw.xhat, bw.part,
                        last ? nullptr : bw.st_xhat, bw, st)) != RS_OK)
       return s;
+    // the kept rows and, unless this is the last block, their LayerNorm statistics
+    const size_t stat_bytes = (size_t)rs::stat_stride(d->C) * 8;
     if ((s = run_select(B, curL, k, d->has_cls, nullptr, bw.part, rs::score_parts(d->C), nullptr,
-                        ws->kept, ids, ids_out, bw.xhat, dst, row_bytes, st)) != RS_OK)
+                        ws->kept, ids, ids_out, bw.xhat, dst, row_bytes, st,
+                        last ? nullptr : bw.st_xhat, last ? nullptr : bw.st_x, stat_bytes)) != RS_OK)
       return s;
-    if (!last) {
-      // the kept rows' LayerNorm statistics follow them
-      const size_t stat_bytes = (size_t)rs::stat_stride(d->C) * 8;
-      RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)stat_bytes, st, [&] {
-        return rs::launch_gather(bw.st_xhat, ws->kept, bw.st_x, B, curL, k, (int)stat_bytes, st);
-      }));
-    }
     cur = dst;
     ids = ids_out;
     curL = k;

@@ -119,13 +119,23 @@ hipError_t launch_attention(Dtype dt, const void* qkv, void* out, int B, int L, 
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
                              hipStream_t stream);
 
-// Per-sample exact top-k.  Score source: `scores` [B][L], or when `part` is not null the
-// fp32 partial sums of squares [B*L][P] (score = sqrt of their sum).  Writes the
-// scores (if scores_out), kept indices ascending [B][k], and (if ids_out) the composed
-// original ids ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.
+// Per-sample exact top-k, one workgroup per sample.  Score source: `scores` [B][L], or
+// when `part` is not null the fp32 partial sums of squares [B*L][P] (score = sqrt of
+// their sum).  Writes the scores (if scores_out), kept indices ascending [B][k], and (if
+// ids_out) the composed original ids ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.
+// Then copies the kept rows of up to two row sets: dst[b][j] = src[b][kept[b][j]], rows
+// of row_bytes (a multiple of 16).
+struct TopkCopy {
+  const void* src;
+  void* dst;
+  int row_bytes;
+};
 hipError_t launch_topk(const float* scores, const float* part, int P, int B, int L, int k,
                        int has_cls, float* scores_out, int32_t* kept, const int32_t* ids_in,
-                       int32_t* ids_out, hipStream_t stream);
+                       int32_t* ids_out, const TopkCopy* copies, int ncopies, hipStream_t stream);
+// Batches at least this large copy the kept rows inside the top-k launch (one workgroup
+// per sample); smaller ones use launch_gather, whose grid spans all rows.
+constexpr int kTopkCopyMinBatch = 32;
 
 // out[b][j][:] = x[b][kept[b][j]][:], rows of row_bytes (multiple of 16).
 hipError_t launch_gather(const void* x, const int32_t* kept, void* out, int B, int L, int k,

@@ -105,18 +105,38 @@ template <typename T>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
                                                     const T* __restrict__ x,
                                                     float* __restrict__ s, int M, int C) {
+  // 16 lanes per row; each lane takes every 16th 8-element chunk.  A row of up to 1024
+  // elements is at most 8 chunks per lane, all requested before any is used, so a lane
+  // waits for memory once per 8 chunks instead of once per chunk.
+  constexpr int U = 8;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
   float acc = 0.f;
   if (row < M) {
     const size_t base = (size_t)row * C;
-    for (int ch = sub; ch < (C >> 3); ch += 16) {
-      float a[8], b[8];
-      load8f(fx + base + ch * 8, a);
-      load8f(x + base + ch * 8, b);
+    const int nch = C >> 3;
+    for (int c0 = 0; c0 < nch; c0 += 16 * U) {
+      Frag8<T> fa[U], fb[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = a[e] - b[e];
-        acc += d * d;
+      for (int u = 0; u < U; ++u) {
+        const int ch = c0 + sub + 16 * u;
+        if (ch < nch) {
+          load_frag(fa[u], fx + base + ch * 8);
+          load_frag(fb[u], x + base + ch * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ch = c0 + sub + 16 * u;
+        if (ch < nch) {
+          float a[8], b[8];
+          frag_to_f32(fa[u], a);
+          frag_to_f32(fb[u], b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float d = a[e] - b[e];
+            acc += d * d;
+          }
+        }
       }
     }
   }
@@ -136,6 +156,18 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kWaveMaxL = 256;
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
 
 // exclusive prefix sum over the 1024 threads of the workgroup
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
@@ -154,14 +186,60 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return before + incl - v;
 }
 
-// One workgroup per sample.  Exact k-th largest key by a 4-pass 8-bit radix select
-// (MSB first) over an LDS histogram, then every key above it plus the lowest-index keys
-// equal to it, emitted in ascending index order.  Integer work only: deterministic.
+// One workgroup per sample.  Selection of the k largest keys (ties to the lower index): the
+// exact k-th largest key T by a 4-pass 8-bit radix select (MSB first) over an LDS
+// histogram; kept = every key above T plus the lowest-index keys equal to it.
+//  - L <= kWaveMaxL: wave 0 alone, 4 keys per lane, lane scans instead of workgroup
+//    barriers (a short row's selection is otherwise all barrier latency).
+//  - longer L: all threads, one histogram pass per 8 bits with workgroup barriers.
+// Kept indices are emitted in ascending index order (block scans), composed with ids_in,
+// and listed in LDS; then the workgroup copies up to two row sets of the kept rows
+// (RowCopy: 16-byte units per row), so selection and compaction are one launch.  Integer
+// work only: deterministic.
+struct RowCopy {
+  const char* src;  // [L] rows of `units` 16-byte units per sample, or null
+  char* dst;        // [k] rows per sample
+  int units;
+};
+
+__device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list, int b, int L, int k) {
+  if (!c.src) return;
+  const int upr = c.units;
+  const u32x4* src = reinterpret_cast<const u32x4*>(c.src) + (long long)b * L * upr;
+  u32x4* dst = reinterpret_cast<u32x4*>(c.dst) + (long long)b * k * upr;
+  constexpr int U = 8;  // rows in flight per thread
+  const int tid = threadIdx.x;
+  if (upr <= kTopkThreads) {
+    // thread -> (row offset r, unit cu), fixed; rows r, r + rpi, r + 2 rpi, ...
+    const int rpi = kTopkThreads / upr, r = tid / upr, cu = tid - r * upr;
+    if (r >= rpi) return;
+    for (int j0 = r; j0 < k; j0 += rpi * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int j = j0 + q * rpi;
+        if (j < k) v[q] = src[(long long)list[j] * upr + cu];
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int j = j0 + q * rpi;
+        if (j < k) dst[(long long)j * upr + cu] = v[q];
+      }
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const u32x4* s = src + (long long)list[j] * upr;
+      u32x4* d = dst + (long long)j * upr;
+      for (int cu = tid; cu < upr; cu += kTopkThreads) d[cu] = s[cu];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, const float* __restrict__ part, int P, int L, int k,
     int has_cls, float* __restrict__ scores_out, int32_t* __restrict__ kept,
-    const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out) {
-  __shared__ uint32_t keys[RS_MAX_TOKENS];
+    const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out, RowCopy c0, RowCopy c1) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[RS_MAX_TOKENS];  // keys, then the kept list
   __shared__ uint32_t hist[256];
   __shared__ int wsum[kTopkThreads / 64];
   __shared__ uint32_t sel[2];
@@ -183,73 +261,153 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   __syncthreads();
 
-  uint32_t prefix = 0u, pmask = 0u;
-  uint32_t krem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    for (int i = tid; i < L; i += kTopkThreads) {
-      const uint32_t key = keys[i];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane covers bins 255-4*tid down to 252-4*tid; counts above run high -> low
-      uint32_t c[4], loc = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * tid - q];
-        loc += c[q];
-      }
-      uint32_t incl = loc;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += t;
-      }
-      uint32_t above = incl - loc;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (above < krem && above + c[q] >= krem) {
-          sel[0] = (uint32_t)(255 - 4 * tid - q);
-          sel[1] = above;
-        }
-        above += c[q];
-      }
-    }
-    __syncthreads();
-    prefix |= sel[0] << shift;
-    pmask |= 0xFFu << shift;
-    krem -= sel[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;  // the k-th largest key; krem of its copies are kept
-
-  const int seg = (L + kTopkThreads - 1) / kTopkThreads;
+  // per-thread segment [i0, i1) and its keep flags (bit i - i0)
+  const int seg = (L + kTopkThreads - 1) / kTopkThreads;  // <= 16
   const int i0 = min(tid * seg, L), i1 = min(i0 + seg, L);
-  int eq = 0;
-  for (int i = i0; i < i1; ++i) eq += keys[i] == T;
-  const int eq_before = block_exclusive_scan(eq, wsum);
-  int cnt = 0, e = eq_before;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
-    const bool keep = key > T || (key == T && (uint32_t)e < krem);
-    e += key == T;
-    cnt += keep;
+  uint32_t keepbits = 0u;
+  if (L <= kWaveMaxL) {
+    // wave 0 alone: lane l holds keys 4l .. 4l + 3
+    if (tid < 64) {
+      const int lane = tid;
+      uint32_t kk[4];
+      bool valid[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        valid[q] = 4 * lane + q < L;
+        kk[q] = valid[q] ? keys[4 * lane + q] : 0u;
+      }
+      uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (valid[q] && (kk[q] & pmask) == prefix) atomicAdd(&hist[(kk[q] >> shift) & 255u], 1u);
+        __builtin_amdgcn_wave_barrier();
+        // lane covers bins 255-4*lane down to 252-4*lane; counts above run high -> low
+        uint32_t c[4], loc = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * lane - q];
+          loc += c[q];
+        }
+        uint32_t above = wave_inclusive_scan(loc) - loc;
+        uint32_t bin = 0u, ab = 0u;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (above < krem && above + c[q] >= krem) {
+            found = true;
+            bin = (uint32_t)(255 - 4 * lane - q);
+            ab = above;
+          }
+          above += c[q];
+        }
+        const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+        bin = __shfl(bin, src, 64);
+        ab = __shfl(ab, src, 64);
+        prefix |= bin << shift;
+        pmask |= 0xFFu << shift;
+        krem -= ab;
+        __builtin_amdgcn_wave_barrier();
+      }
+      const uint32_t T = prefix;  // the k-th largest key; krem of its copies are kept
+      uint32_t eq = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) eq += (valid[q] && kk[q] == T) ? 1u : 0u;
+      uint32_t e = wave_inclusive_scan(eq) - eq;
+      uint32_t keep = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (valid[q] && (kk[q] > T || (kk[q] == T && e < krem))) keep |= 1u << q;
+        e += (valid[q] && kk[q] == T) ? 1u : 0u;
+      }
+      const uint32_t cnt = __builtin_popcount(keep);
+      uint32_t pos = wave_inclusive_scan(cnt) - cnt;
+      int32_t* kb = kept + (size_t)b * k;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (((keep >> q) & 1u) && pos < (uint32_t)k) {
+          const int i = 4 * lane + q;
+          kb[pos] = i;
+          if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+          keys[pos] = (uint32_t)i;  // kept list (the keys were read into registers above)
+          ++pos;
+        }
+      }
+    }
+    if (!c0.src && !c1.src) return;
+    __syncthreads();
+    copy_rows(c0, keys, b, L, k);
+    copy_rows(c1, keys, b, L, k);
+    return;
   }
-  int pos = block_exclusive_scan(cnt, wsum);
-  e = eq_before;
+  {
+    uint32_t prefix = 0u, pmask = 0u;
+    uint32_t krem = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < L; i += kTopkThreads) {
+        const uint32_t key = keys[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane covers bins 255-4*tid down to 252-4*tid; counts above run high -> low
+        uint32_t c[4], loc = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * tid - q];
+          loc += c[q];
+        }
+        uint32_t incl = loc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += t;
+        }
+        uint32_t above = incl - loc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (above < krem && above + c[q] >= krem) {
+            sel[0] = (uint32_t)(255 - 4 * tid - q);
+            sel[1] = above;
+          }
+          above += c[q];
+        }
+      }
+      __syncthreads();
+      prefix |= sel[0] << shift;
+      pmask |= 0xFFu << shift;
+      krem -= sel[1];
+      __syncthreads();
+    }
+    const uint32_t T = prefix;  // the k-th largest key; krem of its copies are kept
+    int eq = 0;
+    for (int i = i0; i < i1; ++i) eq += keys[i] == T;
+    int e = block_exclusive_scan(eq, wsum);
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = keys[i];
+      if (key > T || (key == T && (uint32_t)e < krem)) keepbits |= 1u << (i - i0);
+      e += key == T;
+    }
+  }
+  int pos = block_exclusive_scan(__builtin_popcount(keepbits), wsum);  // also orders keys reads
   int32_t* kb = kept + (size_t)b * k;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
-    const bool keep = key > T || (key == T && (uint32_t)e < krem);
-    e += key == T;
-    if (keep && pos < k) {
+    if (((keepbits >> (i - i0)) & 1u) && pos < k) {
       kb[pos] = i;
       if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+      keys[pos] = (uint32_t)i;  // kept list (every key read above is done: scan barrier)
       ++pos;
     }
   }
+  if (!c0.src && !c1.src) return;
+  __syncthreads();
+  copy_rows(c0, keys, b, L, k);
+  copy_rows(c1, keys, b, L, k);
 }
 
 // ---------------------------------------------------------------- gather
@@ -324,12 +482,15 @@ hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* sco
 
 hipError_t launch_topk(const float* scores, const float* part, int P, int B, int L, int k,
                        int has_cls, float* scores_out, int32_t* kept, const int32_t* ids_in,
-                       int32_t* ids_out, hipStream_t stream) {
+                       int32_t* ids_out, const TopkCopy* copies, int ncopies, hipStream_t stream) {
+  RowCopy c[2] = {{nullptr, nullptr, 0}, {nullptr, nullptr, 0}};
+  for (int i = 0; i < ncopies && i < 2; ++i)
+    c[i] = {static_cast<const char*>(copies[i].src), static_cast<char*>(copies[i].dst),
+            copies[i].row_bytes / 16};
   topk_kernel<<<B, kTopkThreads, 0, stream>>>(scores, part, P, L, k, has_cls, scores_out, kept,
-                                              ids_in, ids_out);
+                                              ids_in, ids_out, c[0], c[1]);
   return hipGetLastError();
 }
-
 hipError_t launch_gather(const void* x, const int32_t* kept, void* out, int B, int L, int k,
                          int row_bytes, hipStream_t stream) {
   const int upr = row_bytes / 16;
