@@ -60,6 +60,19 @@ def cpu_baseline(wl, x, blocks, budget_s=12.0):
 
 
 # device kernel symbol (mangled) -> kernel class of the library's timing interface
+# The pages' throughput for their own settings ("Representation Shift: Unifying Token
+# Compression with FlashAttention", Table 5 for DeiT at batch 512, Tables 2 and 4 for UMT at
+# batch 20 x 12 frames), measured on an NVIDIA RTX A6000 over the whole forward pass
+# (patch embedding and head included) -- context only, not the same work as the encoder
+# timed here, so it is reported beside `vs_baseline` (which stays null).
+PAGES_CONTEXT = {
+    "deit_t512": (13296, "Table 5, DeiT-T, Ours"), "deit_s512": (5948, "Table 5, DeiT-S, Ours"),
+    "deit_b512": (2428, "Table 5, DeiT-B, Ours"), "umt_b12f_ret": (175, "Table 2, UMT-B, Ours"),
+    "umt_l12f_ret": (66, "Table 2, UMT-L, Ours"), "umt_b12f_qa": (128, "Table 4, UMT-B, Ours"),
+    "umt_l12f_qa": (46, "Table 4, UMT-L, Ours"),
+}
+
+
 def kernel_class(mangled: str):
     import re
     # the GEMM and, when K is split, its reduction kernel (which runs the epilogue)
@@ -361,6 +374,11 @@ def main():
         "roofline": roof,
         "kernel_ms_per_step": {k: round(v["ms"], 4) for k, v in per.items()},  # single lane
     }
+    if wl.name in PAGES_CONTEXT:
+        v, cite = PAGES_CONTEXT[wl.name]
+        line["pages_context"] = {"value": v, "unit": f"{wl.unit}/s", "source": cite,
+                                 "note": "RTX A6000, whole forward pass; not the same work",
+                                 "ratio": round(value / v, 2)}
     if args.copy_probe:
         copy_probe(rs, torch)
     if not args.no_cpu_baseline:

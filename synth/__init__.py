@@ -79,6 +79,26 @@ WORKLOADS: Dict[str, Workload] = {
     # UMT-L-shaped video encoder: 4 clips x 1568 tokens, 24 blocks
     "umt_l": Workload("umt_l", 4, 1568, 1024, 16, 4096, 24, "bf16", False,
                       (2, 6, 10, 14), (0.5, 0.5, 0.5, 0.5), "vid"),
+    # The pages' own settings.  DeiT-T/S/B on ImageNet-1K (Sec. 4.2, Table 5): 20 % of the
+    # current tokens dropped after the blocks the pages number 1, 4, 7 (0-based 0, 3, 6);
+    # batch 512 for throughput.
+    "deit_t512": Workload("deit_t512", 512, 197, 192, 3, 768, 12, "bf16", True,
+                          (0, 3, 6), (0.8, 0.8, 0.8), "img"),
+    "deit_s512": Workload("deit_s512", 512, 197, 384, 6, 1536, 12, "bf16", True,
+                          (0, 3, 6), (0.8, 0.8, 0.8), "img"),
+    "deit_b512": Workload("deit_b512", 512, 197, 768, 12, 3072, 12, "bf16", True,
+                          (0, 3, 6), (0.8, 0.8, 0.8), "img"),
+    # UMT-B/L at 12 frames x 196 patches = 2352 tokens, no class token, batch 20 (Sec. 4.1
+    # throughput setting); 20 % (retrieval, Table 2) or 10 % (QA, Table 4) of the current
+    # tokens dropped after each of the first three blocks.
+    "umt_b12f_ret": Workload("umt_b12f_ret", 20, 2352, 768, 12, 3072, 12, "bf16", False,
+                             (0, 1, 2), (0.8, 0.8, 0.8), "vid"),
+    "umt_b12f_qa": Workload("umt_b12f_qa", 20, 2352, 768, 12, 3072, 12, "bf16", False,
+                            (0, 1, 2), (0.9, 0.9, 0.9), "vid"),
+    "umt_l12f_ret": Workload("umt_l12f_ret", 20, 2352, 1024, 16, 4096, 24, "bf16", False,
+                             (0, 1, 2), (0.8, 0.8, 0.8), "vid"),
+    "umt_l12f_qa": Workload("umt_l12f_qa", 20, 2352, 1024, 16, 4096, 24, "bf16", False,
+                            (0, 1, 2), (0.9, 0.9, 0.9), "vid"),
 }
 
 

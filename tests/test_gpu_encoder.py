@@ -18,7 +18,8 @@ from rs_testutil import (check_block_output, check_scores, kept_admissible, spec
 
 pytestmark = pytest.mark.gpu
 
-SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2]}
+SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2],
+           "deit_s512": [511], "umt_l12f_ret": [13]}
 
 
 def lanes(B, L_final):
@@ -86,7 +87,7 @@ def check_encoder(wl, samples):
     print(f"{wl.name} B{wl.B}: exact kept-set agreement {exact}/{total} sampled prune stages")
 
 
-@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l"])
+@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l", "deit_s512", "umt_l12f_ret"])
 def test_encoder_full_size(name):
     check_encoder(synth.WORKLOADS[name], SAMPLED[name])
 
