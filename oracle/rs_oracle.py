@@ -19,6 +19,10 @@ FlashAttention" (arXiv HTML page), in float64 NumPy:
   * Sec. 3.2 (toy experiments) and Sec. 4.1 / 4.2: the tokens with the lowest
     scores are dropped, the same count for every sample, progressively over the
     listed layers.
+  * Sec. 3.3, "Operation choice" and "Distance metrics": the ablation variants of the
+    score -- through the attention sublayer D(SA(LN(x)), x), the MLP sublayer
+    D(MLP(LN(x')), x') (the method) or the whole block D(x_hat, x); with the L2 norm
+    (the method), the L1 norm, or the cosine distance 1 - a.b / (|a| |b|).
 
 Readings taken where the pages leave a step open (each also listed in the design
 notes of the repository):
@@ -29,6 +33,10 @@ notes of the repository):
   * MLP = fc1 (C -> hidden) + GELU (erf form) + fc2 (hidden -> C), both with bias;
   * LayerNorm: biased variance, eps a parameter (1e-6 in every workload);
   * the score subtracts x' from MLP(LN(x')) literally (not x_hat - x');
+  * SA(LN(x)) in the attention variant is the attention sublayer's output, i.e. after
+    the output projection and its bias (the term Eq. (5) adds to x);
+  * cosine distance: 1 - a.b / max(|a| |b|, 1e-8), so a zero vector is at distance 1
+    (the pages give no rule for zero norms);
   * selection: order by score descending, ties to the lower token index, NaN
     lowest, the class token (index 0) always kept when present; kept tokens are
     emitted in ascending original order;
@@ -129,12 +137,18 @@ def multi_head_attention(xn: np.ndarray, w_qkv, b_qkv, heads: int, fused: bool =
 
 # ----------------------------------------------------------------------------- block
 
-def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], heads: int, eps: float = 1e-6,
-                  fused_attention: bool = False) -> Dict[str, np.ndarray]:
-    """One pre-LN block on one sample x [L, C], Eqs. (5) and (6), plus the MLP-sublayer
-    representation shift (Eq. (4), Sec. 3.3 case ii, L2).
+SHIFT_OPS = ("mlp", "attn", "block")
+DISTANCES = ("l2", "l1", "cos")
 
-    Returns x_prime (Eq. 5), mlp (= MLP(LN(x'))), x_hat (Eq. 6) and score [L]."""
+
+def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], heads: int, eps: float = 1e-6,
+                  fused_attention: bool = False, op: str = "mlp",
+                  dist: str = "l2") -> Dict[str, np.ndarray]:
+    """One pre-LN block on one sample x [L, C], Eqs. (5) and (6), plus the representation
+    shift (Eq. (4)) of the chosen operation and distance (Sec. 3.3; the method: MLP, L2).
+
+    Returns x_prime (Eq. 5), sa (= SA(LN(x))), mlp (= MLP(LN(x'))), x_hat (Eq. 6) and
+    score [L]."""
     x = np.asarray(x, F64)
     xn1 = layer_norm(x, w["ln1_g"], w["ln1_b"], eps)
     sa = linear(multi_head_attention(xn1, w["w_qkv"], w["b_qkv"], heads, fused_attention),
@@ -143,14 +157,27 @@ def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], heads: int, eps: floa
     xn2 = layer_norm(x_prime, w["ln2_g"], w["ln2_b"], eps)
     mlp = linear(gelu(linear(xn2, w["w_fc1"], w["b_fc1"])), w["w_fc2"], w["b_fc2"])
     x_hat = mlp + x_prime                                               # Eq. (6)
-    score = representation_shift(mlp, x_prime)                          # Eq. (4), case ii
-    return {"x_prime": x_prime, "mlp": mlp, "x_hat": x_hat, "score": score}
+    # Sec. 3.3 operation choice: (i) attention, (ii) MLP, (iii) the entire block
+    f_x, ref = {"attn": (sa, x), "mlp": (mlp, x_prime), "block": (x_hat, x)}[op]
+    score = representation_shift(f_x, ref, dist)                        # Eq. (4)
+    return {"x_prime": x_prime, "sa": sa, "mlp": mlp, "x_hat": x_hat, "score": score}
 
 
-def representation_shift(f_x: np.ndarray, x: np.ndarray) -> np.ndarray:
-    """Eq. (4) with the L2 distance: per token, || F(x) - x ||_2 over the channel axis."""
-    diff = np.asarray(f_x, F64) - np.asarray(x, F64)
-    return np.sqrt((diff * diff).sum(axis=-1))
+def representation_shift(f_x: np.ndarray, x: np.ndarray, dist: str = "l2") -> np.ndarray:
+    """Eq. (4): per token, D(F(x), x) over the channel axis, D one of the distances of
+    Sec. 3.3: L2 norm of the difference (the method), L1 norm of the difference, or the
+    cosine distance 1 - a.b / (|a| |b|)."""
+    a, b = np.asarray(f_x, F64), np.asarray(x, F64)
+    if dist == "l2":
+        diff = a - b
+        return np.sqrt((diff * diff).sum(axis=-1))
+    if dist == "l1":
+        return np.abs(a - b).sum(axis=-1)
+    if dist == "cos":
+        dot = (a * b).sum(axis=-1)
+        den = np.sqrt((a * a).sum(axis=-1)) * np.sqrt((b * b).sum(axis=-1))
+        return 1.0 - dot / np.maximum(den, 1e-8)
+    raise ValueError(dist)
 
 
 # ----------------------------------------------------------------------------- selection
@@ -199,14 +226,14 @@ def schedule(depth: int, L: int, prune_layers: Sequence[int], keep_ratios: Seque
 
 def encoder_forward(x: np.ndarray, blocks: List[Dict[str, np.ndarray]], heads: int,
                     prune_layers: Sequence[int], keep_ratios: Sequence[float], has_cls: bool,
-                    eps: float = 1e-6):
+                    eps: float = 1e-6, op: str = "mlp", dist: str = "l2"):
     """Blocks in order on one sample; after each listed block keep the top
-    floor(r*L+1/2) tokens by the block's MLP representation shift and compact the
-    block's output to them.  Returns (out [L_final, C], original ids [L_final])."""
+    floor(r*L+1/2) tokens by the block's representation shift (the method: MLP, L2) and
+    compact the block's output to them.  Returns (out [L_final, C], original ids)."""
     cur = np.asarray(x, F64)
     ids = np.arange(cur.shape[0])
     for b, w in enumerate(blocks):
-        r = block_forward(cur, w, heads, eps)
+        r = block_forward(cur, w, heads, eps, op=op, dist=dist)
         cur = r["x_hat"]
         if b in prune_layers:
             k = keep_count(keep_ratios[list(prune_layers).index(b)], cur.shape[0])

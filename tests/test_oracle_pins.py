@@ -189,6 +189,48 @@ def test_zero_attention_keeps_residual():
                                rtol=1e-14)
 
 
+def test_distances_on_crafted_vectors():
+    """Sec. 3.3 distance metrics on vectors whose distances are known by hand."""
+    a = np.array([[3.0, 4.0, 0.0], [1.0, 0.0, 0.0], [2.0, 2.0, 0.0], [1.0, 2.0, 0.0], [0.0, 0.0, 0.0]])
+    b = np.array([[0.0, 0.0, 0.0], [0.0, 1.0, 0.0], [1.0, 1.0, 0.0], [-2.0, -4.0, 0.0], [0.0, 0.0, 0.0]])
+    np.testing.assert_allclose(O.representation_shift(a, b, "l2"), [5.0, 2 ** 0.5, 2 ** 0.5, 45 ** 0.5, 0.0],
+                               rtol=1e-15)
+    np.testing.assert_allclose(O.representation_shift(a, b, "l1"), [7.0, 2.0, 2.0, 9.0, 0.0], rtol=1e-15)
+    # zero vector: distance 1 (reading); orthogonal 1; parallel 0; anti-parallel 2
+    np.testing.assert_allclose(O.representation_shift(a, b, "cos"), [1.0, 1.0, 0.0, 2.0, 1.0], atol=1e-15)
+    assert O.representation_shift(a, b).tolist() == O.representation_shift(a, b, "l2").tolist()
+
+
+def test_operation_variants_closed_forms():
+    """Sec. 3.3 operation choice with zeroed branches: attention branch zero => the
+    attention shift is D(0, x) and the block shift is the size of the MLP output; both
+    branches zero => the block shift is D(x, x)."""
+    wl = _small()
+    x = synth.make_input(wl, 7)[0].astype(np.float64)
+    w = synth.make_block_weights(wl, 0, 7, init="full", zero=("w_proj", "b_proj"))
+    r2 = O.block_forward(x, w, wl.heads, op="attn", dist="l2")
+    np.testing.assert_array_equal(r2["sa"], np.zeros_like(x))
+    np.testing.assert_allclose(r2["score"], np.sqrt((x * x).sum(1)), rtol=1e-13)
+    np.testing.assert_allclose(O.block_forward(x, w, wl.heads, op="attn", dist="l1")["score"],
+                               np.abs(x).sum(1), rtol=1e-13)
+    np.testing.assert_allclose(O.block_forward(x, w, wl.heads, op="attn", dist="cos")["score"], 1.0,
+                               rtol=0, atol=1e-15)
+    # x' = x, x_hat = x + y: the block shift is the size of the MLP output y itself
+    rb = O.block_forward(x, w, wl.heads, op="block", dist="l2")
+    np.testing.assert_allclose(rb["score"], np.sqrt((rb["mlp"] ** 2).sum(1)), rtol=1e-9)
+    np.testing.assert_allclose(O.block_forward(x, w, wl.heads, op="block", dist="l1")["score"],
+                               np.abs(rb["mlp"]).sum(1), rtol=1e-9)
+    w0 = synth.make_block_weights(wl, 0, 7, init="full", zero=("w_proj", "b_proj", "w_fc2", "b_fc2"))
+    np.testing.assert_array_equal(O.block_forward(x, w0, wl.heads, op="block", dist="l2")["score"], 0.0)
+    np.testing.assert_array_equal(O.block_forward(x, w0, wl.heads, op="block", dist="l1")["score"], 0.0)
+    np.testing.assert_allclose(O.block_forward(x, w0, wl.heads, op="block", dist="cos")["score"], 0.0,
+                               atol=1e-15)
+    # with every branch live the three operations differ (a dropped-term slip would not)
+    wf = synth.make_block_weights(wl, 0, 7, init="full")
+    ss = [O.block_forward(x, wf, wl.heads, op=o)["score"] for o in O.SHIFT_OPS]
+    assert not np.allclose(ss[0], ss[1]) and not np.allclose(ss[1], ss[2]) and not np.allclose(ss[0], ss[2])
+
+
 def test_mlp_chain_orientation():
     # fc1 row 2 reads LN channel 1; fc2 row 3 reads hidden unit 2 -> y[:, 3] = GELU(LN(x')[:, 1])
     wl = _small()
