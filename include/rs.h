@@ -52,9 +52,19 @@ typedef enum {
 
 typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
 
+/* Which representation shift scores the tokens (Sec. 3.3, "Operation choice"):
+ * D(F(z), z) through the MLP sublayer, F(z) = MLP(LN(z)) at z = x' (the method), through
+ * the attention sublayer, F = SA(LN(.)) (after the output projection and its bias) at
+ * z = x, or through the whole block, D(x_hat, x). */
+typedef enum { RS_SHIFT_MLP = 0, RS_SHIFT_ATTN = 1, RS_SHIFT_BLOCK = 2 } rs_shift_op;
+/* Distance D per token (Sec. 3.3, "Distance metrics"): L2 norm of the difference (the
+ * method), L1 norm of the difference, or cosine distance 1 - a.b / max(|a| |b|, 1e-8). */
+typedef enum { RS_DIST_L2 = 0, RS_DIST_L1 = 1, RS_DIST_COS = 2 } rs_dist;
+
 /* Shape of one encoder: width C, heads (head dim C/heads = 64), MLP hidden width,
- * LayerNorm epsilon (biased variance), element type, and whether token 0 is a class
- * token that selection always keeps. */
+ * LayerNorm epsilon (biased variance), element type, whether token 0 is a class token
+ * that selection always keeps, and the score (operation and distance; 0, 0 = the
+ * method's MLP-sublayer L2 shift). */
 typedef struct {
   int C;
   int heads;
@@ -62,6 +72,8 @@ typedef struct {
   float ln_eps;
   rs_dtype dtype;
   int has_cls;
+  rs_shift_op score_op;
+  rs_dist score_dist;
 } rs_model_desc;
 
 /* Weights of one pre-LN block (Sec. 3.3, Eqs. (5) and (6)), all of desc.dtype.
@@ -83,7 +95,8 @@ typedef struct {
  *  keep_k   tokens kept per sample, 1 <= keep_k <= L (keep_k == L keeps all; the
  *           class token, when desc->has_cls, counts towards keep_k and is kept).
  *  y        [B][L][C]   block output x_hat (Eq. (6)); nullable (then not written).
- *  scores   [B][L]      fp32 || MLP(LN(x')) - x' ||_2 per token; nullable.
+ *  scores   [B][L]      fp32 per-token shift (desc->score_op, desc->score_dist; the
+ *                       method: || MLP(LN(x')) - x' ||_2); nullable.
  *  kept_idx [B][keep_k] kept token indices of each sample, ascending.  Order used to
  *           choose: score descending, ties to the lower index, NaN lowest.
  *  y_kept   [B][keep_k][C] rows of x_hat at kept_idx (class token first when present).
@@ -97,6 +110,9 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
  * scores[r] = || fx[r,:] - x[r,:] ||_2 for every row r of [B*L][C]. */
 rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
                    float* scores, hipStream_t stream);
+/* Same with the distance of Sec. 3.3 chosen: scores[r] = D(fx[r,:], x[r,:]). */
+rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
+                        rs_dist dist, float* scores, hipStream_t stream);
 
 /* Per-sample selection and compaction: keep the keep_k highest scores of each sample
  * (ties to the lower index, NaN lowest, token 0 always kept if has_cls), write their
@@ -110,7 +126,8 @@ rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C
  * in order; after each block listed in prune_layers (0-based, strictly ascending) the
  * block's output is compacted to the floor(r*L + 1/2) highest-scoring tokens of the
  * current L (r = the matching keep_ratios entry, 0 < r <= 1, evaluated in IEEE
- * double), the score being that block's MLP-sublayer shift.
+ * double), the score being that block's representation shift (desc->score_op,
+ * desc->score_dist).
  *  blocks   [depth] weight sets.
  *  out      [B][L_final][C] encoder output (L_final from rs_encoder_out_len).
  *  out_idx  [B][L_final] original token index of every output row.

@@ -31,15 +31,17 @@ def to_host(t) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
-def spec_of(wl):
+def spec_of(wl, op: str = "mlp", dist: str = "l2"):
     import vit_token_pruning_amd as rs
-    return rs.ModelSpec(wl.C, wl.heads, wl.hidden, torch_dtype(wl.dtype), wl.has_cls, wl.ln_eps)
+    return rs.ModelSpec(wl.C, wl.heads, wl.hidden, torch_dtype(wl.dtype), wl.has_cls, wl.ln_eps,
+                        score_op=op, score_dist=dist)
 
 
-def oracle_block(x: np.ndarray, w, heads: int, eps: float, samples=None):
+def oracle_block(x: np.ndarray, w, heads: int, eps: float, samples=None, op: str = "mlp",
+                 dist: str = "l2"):
     """Oracle block per sample of x [B, L, C] (float64 results stacked)."""
     samples = range(x.shape[0]) if samples is None else samples
-    res = [O.block_forward(x[b], w, heads, eps) for b in samples]
+    res = [O.block_forward(x[b], w, heads, eps, op=op, dist=dist) for b in samples]
     return {k: np.stack([r[k] for r in res]) for k in ("x_prime", "mlp", "x_hat", "score")}
 
 

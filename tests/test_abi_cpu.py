@@ -28,8 +28,8 @@ def test_every_declared_symbol_is_exported(N):
         assert hasattr(N.lib(), n), n
 
 
-def _desc(N, C=384, heads=6, hidden=1536, dtype=1, has_cls=1, eps=1e-6):
-    return N.ModelDesc(C, heads, hidden, eps, dtype, has_cls)
+def _desc(N, C=384, heads=6, hidden=1536, dtype=1, has_cls=1, eps=1e-6, op=0, dist=0):
+    return N.ModelDesc(C, heads, hidden, eps, dtype, has_cls, op, dist)
 
 
 FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
@@ -60,6 +60,9 @@ def test_block_forward_validation(N):
         (dict(desc=_desc(N, hidden=1000)), E_UNS),
         (dict(desc=_desc(N, eps=0.0)), E_ARG),
         (dict(desc=_desc(N, has_cls=2)), E_ARG),
+        (dict(desc=_desc(N, op=3)), E_ARG),                     # unknown score operation
+        (dict(desc=_desc(N, op=-1)), E_ARG),
+        (dict(desc=_desc(N, dist=3)), E_ARG),                   # unknown distance
         (dict(k=0), E_ARG),
         (dict(k=198), E_ARG),
         (dict(L=0, k=1), E_ARG),
@@ -83,6 +86,9 @@ def test_score_and_topk_validation(N):
     assert lib.rs_score(FAKE, FAKE, 2, 10, 100, 1, FAKE, None) == N.RS_ERR_UNSUPPORTED  # C % 8
     assert lib.rs_score(None, FAKE, 2, 10, 64, 1, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_score(FAKE, FAKE, 2, 10, 64, 5, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_score_dist(FAKE, FAKE, 2, 10, 64, 1, 3, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_score_dist(FAKE, FAKE, 2, 10, 100, 1, 1, FAKE, None) == N.RS_ERR_UNSUPPORTED
+    assert lib.rs_score_dist(FAKE, FAKE, 2, 10, 64, 1, 2, None, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 0, 1, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 11, 1, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_topk_gather(FAKE, FAKE, 2, 10, 64, 1, 5, 3, FAKE, FAKE, None) == N.RS_ERR_INVALID_ARG
@@ -149,6 +155,13 @@ def test_workspace_query(N):
     fold = 3 * 384 * 384 * 2
     assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
     assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
+    # the cosine distance keeps three partial sums per 64-column slice instead of one
+    for op in (0, 1, 2):
+        c = _desc(N, op=op, dist=2)
+        l1 = _desc(N, op=op, dist=1)
+        assert lib.rs_workspace_bytes(ctypes.byref(l1), 1, 256, 197) == a
+        extra = lib.rs_workspace_bytes(ctypes.byref(c), 1, 256, 197) - a
+        assert 256 * 197 * 6 * 2 * 4 <= extra < 256 * 197 * 6 * 2 * 4 + 4096   # 6 slices of 64
 
 
 def test_set_max_lanes(N):

@@ -19,21 +19,33 @@ __all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forwar
            "set_max_lanes"]
 
 _DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
+# representation shift variants of the ablations (rs_shift_op, rs_dist of include/rs.h)
+SHIFT_OPS = {"mlp": 0, "attn": 1, "block": 2}
+DISTANCES = {"l2": 0, "l1": 1, "cos": 2}
 
 
 class ModelSpec:
-    """Width, heads (head dim 64), MLP hidden width, LN eps, dtype, class token flag."""
+    """Width, heads (head dim 64), MLP hidden width, LN eps, dtype, class token flag, and
+    the score: score_op "mlp" (the method), "attn" or "block"; score_dist "l2" (the
+    method), "l1" or "cos"."""
 
     def __init__(self, C: int, heads: int, hidden: int, dtype: torch.dtype = torch.bfloat16,
-                 has_cls: bool = True, ln_eps: float = 1e-6):
+                 has_cls: bool = True, ln_eps: float = 1e-6, score_op: str = "mlp",
+                 score_dist: str = "l2"):
         if dtype not in _DT:
             raise TypeError(f"dtype must be float32 or bfloat16, got {dtype}")
+        if score_op not in SHIFT_OPS:
+            raise ValueError(f"score_op must be one of {sorted(SHIFT_OPS)}, got {score_op!r}")
+        if score_dist not in DISTANCES:
+            raise ValueError(f"score_dist must be one of {sorted(DISTANCES)}, got {score_dist!r}")
         self.C, self.heads, self.hidden, self.dtype = C, heads, hidden, dtype
         self.has_cls, self.ln_eps = bool(has_cls), float(ln_eps)
+        self.score_op, self.score_dist = score_op, score_dist
 
     def desc(self) -> N.ModelDesc:
         return N.ModelDesc(self.C, self.heads, self.hidden, self.ln_eps, _DT[self.dtype],
-                           int(self.has_cls))
+                           int(self.has_cls), SHIFT_OPS[self.score_op],
+                           DISTANCES[self.score_dist])
 
     def weight_shapes(self):
         C, Hd = self.C, self.hidden
@@ -99,8 +111,9 @@ def block_forward(spec: ModelSpec, w: Dict[str, torch.Tensor], x: torch.Tensor, 
     return {"y": y, "scores": s, "kept_idx": kept, "y_kept": yk}
 
 
-def score(fx: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
-    """|| fx - x ||_2 per row over the last axis; fx, x [B, L, C] -> [B, L] fp32."""
+def score(fx: torch.Tensor, x: torch.Tensor, dist: str = "l2") -> torch.Tensor:
+    """D(fx, x) per row over the last axis (dist "l2": || fx - x ||_2, "l1", or "cos":
+    cosine distance); fx, x [B, L, C] -> [B, L] fp32."""
     if fx.shape != x.shape or fx.dtype != x.dtype or x.dim() != 3:
         raise ValueError("fx and x must be [B, L, C] tensors of one shape and dtype")
     B, L, C = x.shape
@@ -108,9 +121,16 @@ def score(fx: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
     _dev(x, "x", x.dtype)
     if x.dtype not in _DT:
         raise TypeError("dtype must be float32 or bfloat16")
+    if dist not in DISTANCES:
+        raise ValueError(f"dist must be one of {sorted(DISTANCES)}, got {dist!r}")
     s = torch.empty(B, L, dtype=torch.float32, device=x.device)
-    N.check("rs_score", lib().rs_score(fx.data_ptr(), x.data_ptr(), B, L, C, _DT[x.dtype],
-                                       s.data_ptr(), _stream()))
+    if dist == "l2":
+        N.check("rs_score", lib().rs_score(fx.data_ptr(), x.data_ptr(), B, L, C, _DT[x.dtype],
+                                           s.data_ptr(), _stream()))
+    else:
+        N.check("rs_score_dist", lib().rs_score_dist(fx.data_ptr(), x.data_ptr(), B, L, C,
+                                                     _DT[x.dtype], DISTANCES[dist], s.data_ptr(),
+                                                     _stream()))
     return s
 
 

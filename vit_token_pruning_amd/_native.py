@@ -27,7 +27,8 @@ P_DBL = ctypes.POINTER(c_double)
 
 class ModelDesc(ctypes.Structure):
     _fields_ = [("C", c_int), ("heads", c_int), ("hidden", c_int), ("ln_eps", c_float),
-                ("dtype", c_int), ("has_cls", c_int)]
+                ("dtype", c_int), ("has_cls", c_int), ("score_op", c_int),
+                ("score_dist", c_int)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -57,6 +58,8 @@ def lib():
         "rs_block_forward": (c_int, [P_DESC, P_W, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "rs_score": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+        "rs_score_dist": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                  c_void_p]),
         "rs_topk_gather": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p]),
         "rs_encoder_forward": (c_int, [P_DESC, P_W, c_int, c_void_p, c_int, c_int, P_INT, P_DBL,

@@ -29,6 +29,10 @@ rs_status fail(rs_status s, const std::string& msg) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t esize(rs_dtype dt) { return dt == RS_BF16 ? 2 : 4; }
+// floats of score partials per token: one per 64-column slice and partial quantity
+size_t part_stride(const rs_model_desc& d) {
+  return (size_t)rs::score_parts(d.C) * rs::dist_quantities((int)d.score_dist);
+}
 size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ kernel timing
@@ -76,6 +80,10 @@ rs_status check_desc(const rs_model_desc* d) {
   if (d->hidden % 64 != 0) return fail(RS_ERR_UNSUPPORTED, "hidden % 64 != 0");
   if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps)) return fail(RS_ERR_INVALID_ARG, "ln_eps must be > 0");
   if (d->has_cls != 0 && d->has_cls != 1) return fail(RS_ERR_INVALID_ARG, "has_cls must be 0 or 1");
+  if (d->score_op != RS_SHIFT_MLP && d->score_op != RS_SHIFT_ATTN && d->score_op != RS_SHIFT_BLOCK)
+    return fail(RS_ERR_INVALID_ARG, "unknown score_op");
+  if (d->score_dist != RS_DIST_L2 && d->score_dist != RS_DIST_L1 && d->score_dist != RS_DIST_COS)
+    return fail(RS_ERR_INVALID_ARG, "unknown score_dist");
   return RS_OK;
 }
 
@@ -173,7 +181,7 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
       M * C * e,                                         // xp: x' * gamma2 (fc1 input)
       M * (size_t)d.hidden * e,                          // h: GELU(fc1)
       M * C * e,                                         // xhat: block output
-      M * (size_t)rs::score_parts(d.C) * 4,              // part: score partials
+      M * part_stride(d) * 4,                            // part: score partials
       st, st, st,                                        // slice partials
       rs::kSplitWsBytes,                                 // split-K partial tiles
   };
@@ -319,10 +327,19 @@ rs_status run_row_stats(const rs_model_desc& d, const void* x, float* stats, int
 }
 
 // One block: Eq. (5) then Eq. (6), LayerNorms folded.  st_x holds the slice partials of
-// the rows of x.  The fc2 epilogue writes x_hat to `out`, the score partials to `part`
-// (nullable) and the slice partials of x_hat to `st_out` (nullable; may alias st_x, which
+// the rows of x.  The fc2 epilogue writes x_hat to `out`; the score partials go to `part`
+// (nullable; [M][part_stride], from the projection epilogue for the attention-sublayer
+// shift, from the fc2 epilogue otherwise) and the slice partials of x_hat to `st_out` (nullable; may alias st_x, which
 // nothing reads after the QKV epilogue).  `out` may alias `x` (the fc2 epilogue reads each
 // element of x before it writes it, and nothing reads x after that).
+void set_score(rs::GemmEpiArgs& ep, const rs_model_desc& d, float* part) {
+  ep.part = part;
+  ep.nparts = rs::score_parts(d.C);
+  ep.pstride = (int)part_stride(d);
+  ep.dist = (int)d.score_dist;
+  ep.shift_block = d.score_op == RS_SHIFT_BLOCK;
+}
+
 rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const FoldWs& fw,
                     const void* x, const float* st_x, int B, int L, void* out, float* part,
                     float* st_out, const BlockWs& ws, hipStream_t st) {
@@ -346,6 +363,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
     ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
     ep.split_ws = ws.split;
+    if (part && d.score_op == RS_SHIFT_ATTN) set_score(ep, d, part);
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiProj, ws.o, w.w_proj, M, C, C, ep, st);
     }));
@@ -362,7 +380,8 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
   {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
-    ep.x = x; ep.p = ws.p; ep.part = part; ep.nparts = rs::score_parts(C);
+    ep.x = x; ep.p = ws.p;
+    if (part && d.score_op != RS_SHIFT_ATTN) set_score(ep, d, part);
     ep.stats_out = st_out; ep.C = C;
     ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
@@ -376,11 +395,12 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
 // an optional second row set (x2 -> x2_kept, e.g. the rows' LayerNorm statistics).  Large
 // batches do it in one launch; small ones copy with a separate all-rows grid.
 rs_status run_select(int B, int L, int k, int has_cls, const float* scores, const float* part,
-                     int P, float* scores_out, int32_t* kept, const int32_t* ids_in,
+                     int P, int dist, float* scores_out, int32_t* kept, const int32_t* ids_in,
                      int32_t* ids_out, const void* x, void* x_kept, size_t row_bytes,
                      hipStream_t st, const void* x2 = nullptr, void* x2_kept = nullptr,
                      size_t row_bytes2 = 0) {
-  const double topk_bytes = (double)B * L * 4.0 * (part ? P : 1) + (scores_out ? B * L * 4.0 : 0.0) +
+  const double topk_bytes = (double)B * L * 4.0 * (part ? P * rs::dist_quantities(dist) : 1) +
+                            (scores_out ? B * L * 4.0 : 0.0) +
                             (double)B * k * 4.0 * (ids_out ? 2 : 1);
   rs::TopkCopy cp[2];
   int nc = 0;
@@ -395,8 +415,8 @@ rs_status run_select(int B, int L, int k, int has_cls, const float* scores, cons
   }
   const bool fused = B >= rs::kTopkCopyMinBatch;
   RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes + (fused ? copy_bytes : 0.0), st, [&] {
-    return rs::launch_topk(scores, part, P, B, L, k, has_cls, scores_out, kept, ids_in, ids_out,
-                           cp, fused ? nc : 0, st);
+    return rs::launch_topk(scores, part, P, dist, B, L, k, has_cls, scores_out, kept, ids_in,
+                           ids_out, cp, fused ? nc : 0, st);
   }));
   if (!fused) {
     for (int i = 0; i < nc; ++i) {
@@ -473,7 +493,8 @@ struct LaneRun {
       return s;
     // the kept rows and, unless this is the last block, their LayerNorm statistics
     const size_t stat_bytes = (size_t)rs::stat_stride(d->C) * 8;
-    if ((s = run_select(B, curL, k, d->has_cls, nullptr, bw.part, rs::score_parts(d->C), nullptr,
+    if ((s = run_select(B, curL, k, d->has_cls, nullptr, bw.part, rs::score_parts(d->C),
+                        (int)d->score_dist, nullptr,
                         ws->kept, ids, ids_out, bw.xhat, dst, row_bytes, st,
                         last ? nullptr : bw.st_xhat, last ? nullptr : bw.st_x, stat_bytes)) != RS_OK)
       return s;
@@ -549,14 +570,21 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
                      nullptr, ws.blk, stream)) != RS_OK)
     return s;
   return run_select(B, L, keep_k, desc->has_cls, nullptr, ws.blk.part, rs::score_parts(desc->C),
-                    scores, kept_idx, nullptr, nullptr, xhat, y_kept,
+                    (int)desc->score_dist, scores, kept_idx, nullptr, nullptr, xhat, y_kept,
                     (size_t)desc->C * esize(desc->dtype), stream);
 }
 
 rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype, float* scores,
                    hipStream_t stream) {
+  return rs_score_dist(fx, x, B, L, C, dtype, RS_DIST_L2, scores, stream);
+}
+
+rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
+                        rs_dist dist, float* scores, hipStream_t stream) {
   rs_status s;
   if (dtype != RS_F32 && dtype != RS_BF16) return fail(RS_ERR_INVALID_ARG, "unknown dtype");
+  if (dist != RS_DIST_L2 && dist != RS_DIST_L1 && dist != RS_DIST_COS)
+    return fail(RS_ERR_INVALID_ARG, "unknown dist");
   if (C < 8 || C % 8 != 0) return fail(RS_ERR_UNSUPPORTED, "C must be a positive multiple of 8");
   if ((s = check_BL(B, L, C, C)) != RS_OK) return s;
   if ((s = check_ptr(fx, "fx")) != RS_OK) return s;
@@ -564,7 +592,8 @@ rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype 
   if ((s = check_ptr(scores, "scores")) != RS_OK) return s;
   const int M = B * L;
   RS_HIP(timed(RS_KERNEL_SCORE, (double)M * C * esize(dtype) * 2 + M * 4.0, stream, [&] {
-    return rs::launch_score_rows(dtype == RS_BF16 ? rs::kBF16 : rs::kF32, fx, x, scores, M, C, stream);
+    return rs::launch_score_rows(dtype == RS_BF16 ? rs::kBF16 : rs::kF32, fx, x, scores, M, C,
+                                 (int)dist, stream);
   }));
   return RS_OK;
 }
@@ -585,7 +614,7 @@ rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C
     if ((s = check_ptr(x, "x")) != RS_OK) return s;
     if ((s = check_ptr(x_kept, "x_kept")) != RS_OK) return s;
   }
-  return run_select(B, L, keep_k, has_cls, scores, nullptr, 0, nullptr, kept_idx, nullptr, nullptr, x,
+  return run_select(B, L, keep_k, has_cls, scores, nullptr, 0, 0, nullptr, kept_idx, nullptr, nullptr, x,
                     x_kept, (size_t)C * esize(dtype), stream);
 }
 

@@ -72,6 +72,30 @@ struct Tile {
   static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "loader must divide evenly");
 };
 
+// Representation-shift partials of 8 columns, distance `dist` between a and b (Sec. 3.3
+// "Distance metrics"): 0 L2 -> s0 += sum (a-b)^2; 1 L1 -> s0 += sum |a-b|; 2 cosine ->
+// s0 += a.b, s1 += a.a, s2 += b.b (finished per token after the slices are summed).
+__device__ __forceinline__ void shift_partials(int dist, const float* a, const float* b,
+                                               float& s0, float& s1, float& s2) {
+  if (dist == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = a[e] - b[e];
+      s0 += d * d;
+    }
+  } else if (dist == 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s0 += fabsf(a[e] - b[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s0 += a[e] * b[e];
+      s1 += a[e] * a[e];
+      s2 += b[e] * b[e];
+    }
+  }
+}
+
 // The epilogue of one 128 x 128 output tile, shared by the direct path and the split-K
 // reduction.  `stage(Cs)` writes the tile's fp32 accumulators to LDS as Cs[m][n], with
 // every LDS byte free when it is called.
@@ -176,33 +200,51 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       }
       continue;
     }
-    // kEpiProj / kEpiFc2: the output row in fp32 plus its slice partials
-    float sdev = 0.f;      // fc2: squared representation shift over this thread's columns
+    // kEpiProj / kEpiFc2: the output row in fp32 plus its slice partials, and when scoring
+    // the representation-shift partials of this thread's columns: s0 (L2: sum of squared
+    // differences, L1: sum of |differences|, cosine: sum a.b), s1 and s2 (cosine: a.a, b.b)
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
     float w[8];            // stored values whose slice partials are emitted
     if (ok) {
       float xv[8], pv[8];
       frag_to_f32(px[pass], xv);
       if (EPI == kEpiProj) {
-        float u[8];
+        float u[8], pf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = round_t<T>(v[e] + b8[e]);   // attention branch p, as stored
+          pf[e] = v[e] + b8[e];               // attention branch SA(LN(x)) in fp32
+          pv[e] = round_t<T>(pf[e]);          // ... as stored
           w[e] = xv[e] + pv[e];               // x' (Eq. 5) in fp32: LayerNorm 2 statistics
           u[e] = w[e] * g8[e];                // x' * gamma2: fc1's A operand
         }
         store8f(out + (size_t)m * ep.ldo + n, pv);
         store8f(static_cast<T*>(ep.out2) + (size_t)m * N + n, u);
-      } else {
+        if (ep.part) shift_partials(ep.dist, pf, xv, s0, s1, s2);   // D(SA(LN(x)), x)
+      } else if (ep.dist == 0 && !ep.shift_block) {
+        // the method: || MLP(LN(x')) - x' ||_2
         frag_to_f32(pp[pass], pv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = v[e] + b8[e];   // MLP(LN(x'))
           const float xp = xv[e] + pv[e]; // x' (Eq. 5), re-formed in fp32
           const float d = y - xp;
-          sdev += d * d;
+          s0 += d * d;
           w[e] = round_t<T>(xp + y);      // x_hat (Eq. 6), as stored
         }
         store8f(out + (size_t)m * ep.ldo + n, w);
+      } else {
+        frag_to_f32(pp[pass], pv);
+        float fa[8], fb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = v[e] + b8[e];
+          const float xp = xv[e] + pv[e];
+          fa[e] = ep.shift_block ? xp + y : y;       // x_hat | MLP(LN(x'))
+          fb[e] = ep.shift_block ? xv[e] : xp;       // x     | x'
+          w[e] = round_t<T>(xp + y);
+        }
+        store8f(out + (size_t)m * ep.ldo + n, w);
+        if (ep.part) shift_partials(ep.dist, fa, fb, s0, s1, s2);
       }
     } else {
 #pragma unroll
@@ -225,9 +267,20 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       so[0] = smean;
       so[1] = sm2;
     }
-    if (EPI == kEpiFc2 && ep.part) {
-      sdev = sum8(sdev);
-      if ((sub & 7) == 0 && row_ok) ep.part[(size_t)m * ep.nparts + slice] = sdev;
+    if (ep.part) {
+      s0 = sum8(s0);
+      if (ep.dist == 2) {
+        s1 = sum8(s1);
+        s2 = sum8(s2);
+      }
+      if ((sub & 7) == 0 && row_ok) {
+        float* pr = ep.part + (size_t)m * ep.pstride + slice;
+        pr[0] = s0;
+        if (ep.dist == 2) {
+          pr[ep.nparts] = s1;
+          pr[2 * ep.nparts] = s2;
+        }
+      }
     }
   }
 }

@@ -41,8 +41,14 @@ struct GemmEpiArgs {
   const void* p = nullptr;
   void* out2 = nullptr;        // kEpiProj: x' * gamma2 in the storage type (fc1's A operand)
   const void* gamma = nullptr; // kEpiProj: LayerNorm 2 gamma [N]
-  float* part = nullptr;       // [M][nparts] or null (no scoring)
-  int nparts = 0;
+  // representation-shift partials per 64-column slice, or null (no scoring): kEpiProj
+  // the attention-sublayer shift D(p, x), kEpiFc2 the MLP-sublayer D(y, x') or, with
+  // shift_block, the whole-block D(x_hat, x).  part [M][pstride]; quantity q of slice s at
+  // q * nparts + s: L2 sum of squares, L1 sum of magnitudes, cosine (a.b, a.a, b.b).
+  float* part = nullptr;
+  int nparts = 0, pstride = 0;
+  int dist = 0;                // 0 L2, 1 L1, 2 cosine
+  int shift_block = 0;
   // folded LayerNorm of the A operand rows (kEpiQKV, kEpiGelu)
   const float* stats_in = nullptr;  // [M][stat_stride] float2 slice partials
   const float* fold_c = nullptr;    // [N]
@@ -115,14 +121,15 @@ hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStrea
 hipError_t launch_attention(Dtype dt, const void* qkv, void* out, int B, int L, int H,
                             hipStream_t stream);
 
-// scores[r] = || fx[r] - x[r] ||_2 over C.
+// scores[r] = D(fx[r], x[r]) over C; dist 0 L2, 1 L1, 2 cosine.
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
-                             hipStream_t stream);
+                             int dist, hipStream_t stream);
 
 // Per-sample exact top-k, one workgroup per sample.  Score source: `scores` [B][L], or
-// when `part` is not null the fp32 partial sums of squares [B*L][P] (score = sqrt of
-// their sum).  Writes the scores (if scores_out), kept indices ascending [B][k], and (if
-// ids_out) the composed original ids ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.
+// when `part` is not null the fp32 shift partials [B*L][dist_quantities(dist)][P] of the
+// GEMM epilogues, finished per distance (L2: sqrt of the sum; L1: the sum; cosine:
+// 1 - sum(a.b) / max(sqrt(sum a.a) sqrt(sum b.b), 1e-8)).  Writes the scores (if
+// scores_out), kept indices ascending [B][k], and (if ids_out) the composed original ids ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.
 // Then copies the kept rows of up to two row sets: dst[b][j] = src[b][kept[b][j]], rows
 // of row_bytes (a multiple of 16).
 struct TopkCopy {
@@ -130,9 +137,12 @@ struct TopkCopy {
   void* dst;
   int row_bytes;
 };
-hipError_t launch_topk(const float* scores, const float* part, int P, int B, int L, int k,
-                       int has_cls, float* scores_out, int32_t* kept, const int32_t* ids_in,
-                       int32_t* ids_out, const TopkCopy* copies, int ncopies, hipStream_t stream);
+hipError_t launch_topk(const float* scores, const float* part, int P, int dist, int B, int L,
+                       int k, int has_cls, float* scores_out, int32_t* kept,
+                       const int32_t* ids_in, int32_t* ids_out, const TopkCopy* copies,
+                       int ncopies, hipStream_t stream);
+// partial quantities per slice of each distance (cosine: a.b, a.a, b.b)
+inline int dist_quantities(int dist) { return dist == 2 ? 3 : 1; }
 // Batches at least this large copy the kept rows inside the top-k launch (one workgroup
 // per sample); smaller ones use launch_gather, whose grid spans all rows.
 constexpr int kTopkCopyMinBatch = 32;

@@ -4,7 +4,7 @@
 //
 // Method: "Representation Shift: Unifying Token Compression with FlashAttention" (arXiv
 // HTML).  LayerNorm is the LN of Sec. 3.3, Eqs. (5) and (6); the score is Eq. (4) with
-// the L2 distance (Sec. 3.2); selection drops the lowest-scoring tokens, the same
+// the L2 distance (Sec. 3.2) or the L1 / cosine distances of Sec. 3.3; selection drops the lowest-scoring tokens, the same
 // count in every sample, yielding the reduced set x~ of Sec. 3.1.
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
@@ -100,17 +100,26 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
 }
 
 // ---------------------------------------------------------------- standalone score
-// 16 lanes per row: || fx - x ||_2 accumulated in fp32.
+// Distance of one token's two rows from its accumulated sums: L2 sqrt(s0); L1 s0; cosine
+// 1 - s0 / max(sqrt(s1) sqrt(s2), 1e-8) with s0 = a.b, s1 = a.a, s2 = b.b.
+__device__ __forceinline__ float finish_dist(int dist, float s0, float s1, float s2) {
+  if (dist == 0) return sqrtf(s0);
+  if (dist == 1) return s0;
+  return 1.0f - s0 / fmaxf(sqrtf(s1) * sqrtf(s2), 1e-8f);
+}
+
+// 16 lanes per row: D(fx, x) accumulated in fp32.
 template <typename T>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
                                                     const T* __restrict__ x,
-                                                    float* __restrict__ s, int M, int C) {
+                                                    float* __restrict__ s, int M, int C,
+                                                    int dist) {
   // 16 lanes per row; each lane takes every 16th 8-element chunk.  A row of up to 1024
   // elements is at most 8 chunks per lane, all requested before any is used, so a lane
   // waits for memory once per 8 chunks instead of once per chunk.
   constexpr int U = 8;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
-  float acc = 0.f;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f;
   if (row < M) {
     const size_t base = (size_t)row * C;
     const int nch = C >> 3;
@@ -131,17 +140,33 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
           float a[8], b[8];
           frag_to_f32(fa[u], a);
           frag_to_f32(fb[u], b);
+          if (dist == 0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float d = a[e] - b[e];
-            acc += d * d;
+            for (int e = 0; e < 8; ++e) {
+              const float d = a[e] - b[e];
+              s0 += d * d;
+            }
+          } else if (dist == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s0 += fabsf(a[e] - b[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              s0 += a[e] * b[e];
+              s1 += a[e] * a[e];
+              s2 += b[e] * b[e];
+            }
           }
         }
       }
     }
   }
-  acc = sum16(acc);
-  if (sub == 0 && row < M) s[row] = sqrtf(acc);
+  s0 = sum16(s0);
+  if (dist == 2) {
+    s1 = sum16(s1);
+    s2 = sum16(s2);
+  }
+  if (sub == 0 && row < M) s[row] = finish_dist(dist, s0, s1, s2);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -236,8 +261,8 @@ __device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float* __restrict__ scores, const float* __restrict__ part, int P, int L, int k,
-    int has_cls, float* __restrict__ scores_out, int32_t* __restrict__ kept,
+    const float* __restrict__ scores, const float* __restrict__ part, int P, int dist, int L,
+    int k, int has_cls, float* __restrict__ scores_out, int32_t* __restrict__ kept,
     const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out, RowCopy c0, RowCopy c1) {
   __shared__ __attribute__((aligned(16))) uint32_t keys[RS_MAX_TOKENS];  // keys, then the kept list
   __shared__ uint32_t hist[256];
@@ -249,10 +274,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   for (int i = tid; i < L; i += kTopkThreads) {
     float s;
     if (part) {
-      const float* pp = part + (rb + i) * P;
-      float a = 0.f;
+      // the token's slice partials: quantity q of slice p at q * P + p
+      const float* pp = part + (rb + i) * (size_t)(dist == 2 ? 3 * P : P);
+      float a = 0.f, aa = 0.f, bb = 0.f;
       for (int q = 0; q < P; ++q) a += pp[q];
-      s = sqrtf(a);
+      if (dist == 2)
+        for (int q = 0; q < P; ++q) {
+          aa += pp[P + q];
+          bb += pp[2 * P + q];
+        }
+      s = finish_dist(dist, a, aa, bb);
     } else {
       s = scores[rb + i];
     }
@@ -469,26 +500,27 @@ hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStrea
 }
 
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
-                             hipStream_t stream) {
+                             int dist, hipStream_t stream) {
   const int grid = (M + 15) / 16;
   if (dt == kBF16)
     score_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(fx),
-                                                 static_cast<const bf16*>(x), scores, M, C);
+                                                 static_cast<const bf16*>(x), scores, M, C, dist);
   else
     score_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(fx),
-                                                  static_cast<const float*>(x), scores, M, C);
+                                                  static_cast<const float*>(x), scores, M, C, dist);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* scores, const float* part, int P, int B, int L, int k,
-                       int has_cls, float* scores_out, int32_t* kept, const int32_t* ids_in,
-                       int32_t* ids_out, const TopkCopy* copies, int ncopies, hipStream_t stream) {
+hipError_t launch_topk(const float* scores, const float* part, int P, int dist, int B, int L,
+                       int k, int has_cls, float* scores_out, int32_t* kept,
+                       const int32_t* ids_in, int32_t* ids_out, const TopkCopy* copies,
+                       int ncopies, hipStream_t stream) {
   RowCopy c[2] = {{nullptr, nullptr, 0}, {nullptr, nullptr, 0}};
   for (int i = 0; i < ncopies && i < 2; ++i)
     c[i] = {static_cast<const char*>(copies[i].src), static_cast<char*>(copies[i].dst),
             copies[i].row_bytes / 16};
-  topk_kernel<<<B, kTopkThreads, 0, stream>>>(scores, part, P, L, k, has_cls, scores_out, kept,
-                                              ids_in, ids_out, c[0], c[1]);
+  topk_kernel<<<B, kTopkThreads, 0, stream>>>(scores, part, P, dist, L, k, has_cls, scores_out,
+                                              kept, ids_in, ids_out, c[0], c[1]);
   return hipGetLastError();
 }
 hipError_t launch_gather(const void* x, const int32_t* kept, void* out, int B, int L, int k,
