@@ -29,7 +29,7 @@ METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roof
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
                 "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm", "gather": "hbm",
-                "score": "hbm"}
+                "score": "hbm", "patch_embed": "mfma", "head": "mfma"}
 
 
 def log(*a):
@@ -78,9 +78,11 @@ def kernel_class(mangled: str):
     # the GEMM and, when K is split, its reduction kernel (which runs the epilogue)
     m = re.search(r"(?:gemm_kernel|splitk_reduce_kernel)I(DF16b|f)Li(\d)E", mangled)
     if m:
-        return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score"}[m.group(2)]
+        return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score", "4": "patch_embed",
+                "5": "head"}[m.group(2)]
     for key, name in (("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
-                      ("topk_kernel", "topk"), ("gather_kernel", "gather"), ("score_kernel", "score")):
+                      ("topk_kernel", "topk"), ("gather_kernel", "gather"), ("score_kernel", "score"),
+                      ("cls_rows_kernel", "patch_embed"), ("pool_kernel", "head")):
         if key in mangled:
             return name
     return None
@@ -235,6 +237,47 @@ def standalone(wl, steps):
     return out
 
 
+def whole_forward(wl, spec, blocks, steps, rs, torch):
+    """Context, not `value`: the whole forward pass (patch embedding, the same pruned
+    encoder, final LayerNorm and head) from pixels resident in HBM, as the pages'
+    throughput figures count it.  Synthetic 224 x 224 pixels, 16 x 16 patches."""
+    import synth
+    dt = spec.dtype
+    g = synth.geometry(wl)
+    img = rs.ImageSpec(g.frames, g.in_chans, g.height, g.width, g.patch)
+    dev = lambda a: torch.from_numpy(a).cuda().to(dt)
+    images = dev(synth.make_images(wl, g, 0))
+    emb = {k: dev(v) for k, v in synth.make_embed_weights(wl, g, 0).items()}
+    hw = {k: dev(v) for k, v in synth.make_head_weights(wl, g, 0).items()}
+    vit = rs.ViT(spec, img, emb, blocks, hw, g.pool, wl.B, wl.prune_layers, wl.keep_ratios)
+    for _ in range(3):
+        vit.forward(images)
+    n = max(5, min(steps, 20))
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n):
+        vit.forward(images)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    per = {}
+    for kname in ("patch_embed", "head"):
+        with rs.KernelTimer(kname) as kt:
+            vit.forward(images)
+        per[kname] = {"ms": round(kt.total_ms, 4), "launches": kt.launches,
+                      "tflops": round(kt.work / (kt.total_ms / 1e3) / 1e12, 1) if kt.total_ms else None}
+    torch.cuda.synchronize()
+    value = wl.B / (ms / 1e3)
+    log(f"whole forward ({g.frames} x {g.height}x{g.width} px, patch {g.patch}, head {g.n_out}, "
+        f"{g.pool} pool): {ms:.4f} ms/step, {value:.1f} {wl.unit}/s; {per}")
+    return {"value": round(value, 2), "unit": f"{wl.unit}/s", "ms_per_step": round(ms, 4),
+            "steps": n, "frames": g.frames, "pixels": [g.height, g.width], "patch": g.patch,
+            "n_out": g.n_out, "pool": g.pool, "kernels": per,
+            "note": "patch embedding + the pruned encoder + final LN + head; context only"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +294,8 @@ def main():
     ap.add_argument("--kernel", default="fc1", choices=[k for k in ("ln_prep", "qkv", "attention",
                     "proj", "fc1", "fc2_score", "topk", "gather")],
                     help="roofline kernel when --no-breakdown is given")
+    ap.add_argument("--no-whole", action="store_true",
+                    help="skip the whole-forward context (patch embedding + encoder + head)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB copy through the gather kernel (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -306,7 +351,7 @@ def main():
     else:
         rs.set_max_lanes(1)
         for kname in rs.KERNELS:
-            if kname == "score":
+            if kname in ("score", "patch_embed", "head"):   # not launched by the encoder
                 continue
             with rs.KernelTimer(kname) as kt:
                 enc.forward(x)
@@ -379,6 +424,11 @@ def main():
         line["pages_context"] = {"value": v, "unit": f"{wl.unit}/s", "source": cite,
                                  "note": "RTX A6000, whole forward pass; not the same work",
                                  "ratio": round(value / v, 2)}
+    if not (args.no_whole or args.no_breakdown):
+        line["whole_forward"] = whole_forward(wl, spec, blocks, args.steps, rs, torch)
+        if wl.name in PAGES_CONTEXT:
+            line["pages_context"]["ratio_whole_forward"] = round(
+                line["whole_forward"]["value"] / PAGES_CONTEXT[wl.name][0], 2)
     if args.copy_probe:
         copy_probe(rs, torch)
     if not args.no_cpu_baseline:

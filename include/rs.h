@@ -27,7 +27,8 @@
  *    rs_last_error() returns a message for the calling thread's last failure.
  *  - Calls are re-entrant; concurrent calls need distinct workspaces and outputs.
  *  - Limits (else RS_ERR_UNSUPPORTED): head dim 64 (C == heads*64), C % 64 == 0,
- *    hidden % 64 == 0, 1 <= L <= RS_MAX_TOKENS, and B*L*max(3C, hidden) < 2^31.
+ *    C <= RS_MAX_WIDTH, hidden % 64 == 0, 1 <= L <= RS_MAX_TOKENS, and
+ *    B*L*max(3C, hidden) < 2^31.
  */
 #ifndef RS_H_
 #define RS_H_
@@ -41,6 +42,7 @@ extern "C" {
 #endif
 
 #define RS_MAX_TOKENS 16384
+#define RS_MAX_WIDTH 1024
 
 typedef enum {
   RS_OK = 0,
@@ -145,6 +147,91 @@ rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* 
                              void* out, int32_t* out_idx,
                              void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- the steps either side of the encoder --------------------------------------------
+ * Tokenisation (Sec. 3.1): an H x W image is cut into N = (H/P)(W/P) patches of P x P
+ * pixels; a clip of `frames` images is tokenised frame by frame.  The patch embedding is
+ * the P x P, stride-P convolution with bias, computed as one GEMM whose A operand is
+ * gathered from the images inside the kernel; tokens are the patches in raster order of
+ * the grid, frame after frame, preceded by the class token when desc->has_cls, plus a
+ * position table.  The encoder output ends in a final LayerNorm, a pooling (the class
+ * token's row, or the mean over tokens) and a Linear head.  The pages run these steps
+ * unchanged from the DeiT / UMT models; they bracket the pruned encoder in a whole
+ * forward pass. */
+
+/* Pixel input geometry.  frames >= 1 (1 for an image), in_chans >= 1, patch P in
+ * {8, 16, 32}, height and width positive multiples of P.  Tokens per sample:
+ * L = desc->has_cls + frames * (height/P) * (width/P). */
+typedef struct {
+  int frames;
+  int in_chans;
+  int height;
+  int width;
+  int patch;
+} rs_image_desc;
+
+/* Patch embedding weights, all of desc->dtype:
+ *  w_patch [C][in_chans*P*P]  the convolution weight, each output channel's kernel
+ *                             flattened as (input channel, row, column);
+ *  b_patch [C];
+ *  cls     [C]   class token (read only when desc->has_cls; may be null otherwise);
+ *  pos     [L][C] position table, row 0 the class token's when present. */
+typedef struct {
+  const void* w_patch;
+  const void* b_patch;
+  const void* cls;
+  const void* pos;
+} rs_embed_weights;
+
+typedef enum { RS_POOL_CLS = 0, RS_POOL_MEAN = 1 } rs_pool;
+
+/* Final LayerNorm (ln_g, ln_b [C], eps = desc->ln_eps) and head (w_head [n_out][C],
+ * b_head [n_out]), all of desc->dtype; n_out >= 8 and n_out % 8 == 0.  pool:
+ * RS_POOL_CLS takes token 0's normalised row (requires desc->has_cls), RS_POOL_MEAN the
+ * mean of all tokens' normalised rows. */
+typedef struct {
+  const void* ln_g;
+  const void* ln_b;
+  const void* w_head;
+  const void* b_head;
+  int n_out;
+  rs_pool pool;
+} rs_head_weights;
+
+/* Patch embedding: images [B][frames][in_chans][height][width] (desc->dtype) ->
+ * tokens [B][L][C].  No workspace. */
+rs_status rs_patch_embed(const rs_model_desc* desc, const rs_image_desc* img,
+                         const rs_embed_weights* emb, const void* images, int B,
+                         void* tokens, hipStream_t stream);
+
+/* Final LayerNorm, pooling and head of x [B][L][C]: features [B][C] (the pooled,
+ * normalised, affine-transformed row, desc->dtype) and logits [B][n_out] (desc->dtype).
+ * workspace/ws_bytes >= rs_head_workspace_bytes(B, L, C): fp32 partial sums of the
+ * pooling over blocks of rows. */
+rs_status rs_head(const rs_model_desc* desc, const rs_head_weights* head, const void* x,
+                  int B, int L, void* features, void* logits, void* workspace, size_t ws_bytes,
+                  hipStream_t stream);
+/* Host only: workspace bytes of rs_head (0 for sizes outside the limits). */
+size_t rs_head_workspace_bytes(int B, int L, int C);
+
+/* Whole forward pass: rs_patch_embed, then rs_encoder_forward with the schedule, then
+ * rs_head on the encoder output (whose class token, when present, is its row 0); equal
+ * bit for bit to that chain of calls.  The first block's LayerNorm statistics come from
+ * the patch embedding's epilogue.
+ *  features [B][C], logits [B][n_out]: as rs_head.
+ *  out_idx  [B][L_final] original token index of every encoder output row; nullable.
+ *  workspace/ws_bytes   >= rs_vit_workspace_bytes(desc, img, depth, B). */
+rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
+                         const rs_embed_weights* emb, const rs_block_weights* blocks, int depth,
+                         const rs_head_weights* head, const void* images, int B,
+                         const int* prune_layers, const double* keep_ratios, int n_prune,
+                         void* features, void* logits, int32_t* out_idx,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Host only: workspace bytes that suffice for rs_vit_forward at batch B (any schedule).
+ * Returns 0 for an invalid description or geometry. */
+size_t rs_vit_workspace_bytes(const rs_model_desc* desc, const rs_image_desc* img, int depth,
+                              int B);
+
 /* Host only: token count after the schedule (same rule as rs_encoder_forward). */
 rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers,
                              const double* keep_ratios, int n_prune, int* L_final);
@@ -183,7 +270,9 @@ typedef enum {
   RS_KERNEL_TOPK = 6,
   RS_KERNEL_GATHER = 7,
   RS_KERNEL_SCORE = 8,
-  RS_KERNEL_COUNT = 9
+  RS_KERNEL_PATCH = 9,        /* patch-embedding GEMM and class-token rows */
+  RS_KERNEL_HEAD = 10,        /* final LayerNorm + pooling, and the head GEMM */
+  RS_KERNEL_COUNT = 11
 } rs_kernel_id;
 
 rs_status rs_timing_begin(int kernel_id);

@@ -23,6 +23,9 @@ FlashAttention" (arXiv HTML page), in float64 NumPy:
     score -- through the attention sublayer D(SA(LN(x)), x), the MLP sublayer
     D(MLP(LN(x')), x') (the method) or the whole block D(x_hat, x); with the L2 norm
     (the method), the L1 norm, or the cosine distance 1 - a.b / (|a| |b|).
+  * Sec. 3.1: an H x W image is cut into N = (H/P)(W/P) patches of P x P pixels, the
+    tokens the encoder runs on; the model ends in a final LayerNorm and a linear head
+    (the DeiT and UMT models the pages run unchanged).
 
 Readings taken where the pages leave a step open (each also listed in the design
 notes of the repository):
@@ -42,7 +45,15 @@ notes of the repository):
     emitted in ascending original order;
   * schedule: pruning at block b uses block b's MLP score and compacts block b's
     output; the kept count is floor(r * L + 1/2) of the current L (counting the
-    class token), evaluated in IEEE double.
+    class token), evaluated in IEEE double;
+  * patch embedding: a P x P, stride-P convolution with bias, i.e. each patch
+    flattened channel-major (channel, row, column) times a [C][Cin*P*P] weight; tokens
+    in raster order of the patch grid, frame by frame for video (frame-major); a
+    learned class token first when present; a learned position table [L][C] added to
+    every token (class token included);
+  * head: the final LayerNorm of every token, then the class token's normalised row
+    (image models with a class token) or the mean of all tokens' normalised rows
+    (video models), then a Linear with bias.
 
 Parity status: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (closed forms, textbook identities, brute force on
@@ -241,6 +252,61 @@ def encoder_forward(x: np.ndarray, blocks: List[Dict[str, np.ndarray]], heads: i
             cur = cur[kept]
             ids = ids[kept]
     return cur, ids
+
+
+# ----------------------------------------------------------------------------- around the encoder
+
+def patch_embed(images: np.ndarray, w_patch: np.ndarray, b_patch: np.ndarray,
+                cls: np.ndarray, pos: np.ndarray, patch: int) -> np.ndarray:
+    """Tokens of one sample (Sec. 3.1).  images [T][Cin][H][W] (T = 1 for an image);
+    each P x P patch, flattened as (channel, row, column), times w_patch [C][Cin*P*P]
+    plus b_patch; patches in raster order within a frame, frames in order; the class
+    token `cls` [C] (or None) first; pos [L][C] added to every token."""
+    img = np.asarray(images, F64)
+    T, cin, H, W = img.shape
+    P = int(patch)
+    if H % P or W % P:
+        raise ValueError("image size must be a multiple of the patch size")
+    rows = []
+    for t in range(T):
+        for pr in range(H // P):
+            for pc in range(W // P):
+                rows.append(img[t, :, pr * P:(pr + 1) * P, pc * P:(pc + 1) * P].reshape(-1))
+    tokens = linear(np.stack(rows), w_patch, b_patch)
+    if cls is not None:
+        tokens = np.concatenate([np.asarray(cls, F64)[None, :], tokens], axis=0)
+    pos = np.asarray(pos, F64)
+    if pos.shape != tokens.shape:
+        raise ValueError(f"position table {pos.shape} does not match tokens {tokens.shape}")
+    return tokens + pos
+
+
+def head(x: np.ndarray, ln_g: np.ndarray, ln_b: np.ndarray, w_head: np.ndarray,
+         b_head: np.ndarray, pool: str, eps: float = 1e-6):
+    """Final LayerNorm, pooling and linear head of one sample x [L][C].  pool "cls":
+    the normalised row of token 0; "mean": the mean over tokens of the normalised rows.
+    Returns (features [C], logits [n_out])."""
+    xn = layer_norm(np.asarray(x, F64), ln_g, ln_b, eps)
+    if pool == "cls":
+        feat = xn[0]
+    elif pool == "mean":
+        feat = xn.mean(axis=0)
+    else:
+        raise ValueError(pool)
+    return feat, linear(feat[None, :], w_head, b_head)[0]
+
+
+def vit_forward(images: np.ndarray, emb: Dict[str, np.ndarray], blocks: List[Dict[str, np.ndarray]],
+                hd: Dict[str, np.ndarray], heads: int, patch: int, prune_layers: Sequence[int],
+                keep_ratios: Sequence[float], has_cls: bool, pool: str, eps: float = 1e-6,
+                op: str = "mlp", dist: str = "l2"):
+    """The whole forward pass of one sample: patch embedding, the pruned encoder, the
+    head.  Returns (features, logits, ids of the encoder's output tokens)."""
+    x = patch_embed(images, emb["w_patch"], emb["b_patch"], emb["cls"] if has_cls else None,
+                    emb["pos"], patch)
+    out, ids = encoder_forward(x, blocks, heads, prune_layers, keep_ratios, has_cls, eps, op, dist)
+    feat, logits = head(out, hd["ln_g"], hd["ln_b"], hd["w_head"], hd["b_head"], pool, eps)
+    return feat, logits, ids
 
 
 # ----------------------------------------------------------------------------- work model

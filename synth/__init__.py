@@ -23,7 +23,13 @@ Recipe (identical for every workload unless stated):
     widens the score distribution so that near-ties become rare;
   * bf16 workloads: values are drawn in fp32 and rounded to bf16 (round to
     nearest, ties to even) here, so the GPU path and the oracle see the very same
-    numbers; arrays are returned as float32 holding bf16-representable values.
+    numbers; arrays are returned as float32 holding bf16-representable values;
+  * whole forward pass: pixels ~ N(0, 1) (images after per-channel normalisation),
+    patch weights ~ N(0, 0.02^2), class token and position table ~ N(0, 0.02^2),
+    head weights ~ N(0, 0.02^2), final LayerNorm as the blocks' (``init``);
+    geometry 224 x 224 pixels, 16 x 16 patches, 3 channels, frames = the workload's
+    patch tokens / 196; 1000 classes and class-token pooling for image workloads,
+    a 512-wide head and mean pooling for video workloads.
 """
 from __future__ import annotations
 
@@ -39,6 +45,9 @@ WEIGHT_NAMES = (
 )
 _INPUT_BLOCK_TAG = 1_000_000
 _SPREAD_TAG = 1_000_001
+_IMAGE_TAG = 1_000_002
+_EMBED_TAG = 1_000_003
+_HEAD_TAG = 1_000_004
 
 
 @dataclasses.dataclass(frozen=True)
@@ -161,6 +170,75 @@ def make_block_weights(wl: Workload, block: int, seed: int = 0, init: str = "pap
                  else 0.02 * rng.standard_normal(shp, dtype=np.float32))
         if name in zero:
             a = np.zeros(shp, np.float32)
+        out[name] = _finish(a, wl.dtype)
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    """Pixel input and head of a whole forward pass (data only)."""
+    frames: int
+    in_chans: int
+    height: int
+    width: int
+    patch: int
+    n_out: int
+    pool: str              # "cls" or "mean"
+
+    def tokens(self, has_cls: bool) -> int:
+        return int(has_cls) + self.frames * (self.height // self.patch) * (self.width // self.patch)
+
+
+def geometry(wl: Workload) -> Geometry:
+    """224 x 224 images cut into 16 x 16 patches (196 per frame); the frame count follows
+    from the workload's token count."""
+    patches = wl.L - int(wl.has_cls)
+    if patches % 196:
+        raise ValueError(f"{wl.name}: {patches} patch tokens is not a whole number of frames")
+    return Geometry(patches // 196, 3, 224, 224, 16, 1000 if wl.has_cls else 512,
+                    "cls" if wl.has_cls else "mean")
+
+
+def make_images(wl: Workload, geom: Geometry, seed: int = 0, B: Optional[int] = None) -> np.ndarray:
+    """Pixels [B][frames][in_chans][H][W] ~ N(0, 1)."""
+    B = wl.B if B is None else B
+    rng = np.random.default_rng([seed, _IMAGE_TAG, 0])
+    shape = (B, geom.frames, geom.in_chans, geom.height, geom.width)
+    return _finish(rng.standard_normal(shape, dtype=np.float32), wl.dtype)
+
+
+def make_embed_weights(wl: Workload, geom: Geometry, seed: int = 0) -> Dict[str, np.ndarray]:
+    """w_patch [C][in_chans*P*P], b_patch [C], cls [C], pos [L][C]."""
+    C, L = wl.C, geom.tokens(wl.has_cls)
+    shapes = {"w_patch": (C, geom.in_chans * geom.patch ** 2), "b_patch": (C,), "cls": (C,),
+              "pos": (L, C)}
+    out = {}
+    for tid, (name, shp) in enumerate(shapes.items()):
+        rng = np.random.default_rng([seed, _EMBED_TAG, tid])
+        out[name] = _finish(rng.standard_normal(shp, dtype=np.float32) * np.float32(0.02), wl.dtype)
+    return out
+
+
+def make_head_weights(wl: Workload, geom: Geometry, seed: int = 0, init: str = "paper") -> Dict[str, np.ndarray]:
+    """ln_g, ln_b [C], w_head [n_out][C], b_head [n_out]."""
+    if init not in ("paper", "full"):
+        raise ValueError(init)
+    C, n = wl.C, geom.n_out
+    out = {}
+    for tid, (name, shp) in enumerate((("ln_g", (C,)), ("ln_b", (C,)), ("w_head", (n, C)),
+                                       ("b_head", (n,)))):
+        rng = np.random.default_rng([seed, _HEAD_TAG, tid])
+        if name == "w_head":
+            a = rng.standard_normal(shp, dtype=np.float32) * np.float32(0.02)
+        elif name == "ln_g":
+            a = (np.ones(shp, np.float32) if init == "paper"
+                 else 1.0 + 0.1 * rng.standard_normal(shp, dtype=np.float32))
+        elif name == "ln_b":
+            a = (np.zeros(shp, np.float32) if init == "paper"
+                 else 0.1 * rng.standard_normal(shp, dtype=np.float32))
+        else:
+            a = (np.zeros(shp, np.float32) if init == "paper"
+                 else 0.02 * rng.standard_normal(shp, dtype=np.float32))
         out[name] = _finish(a, wl.dtype)
     return out
 

@@ -192,3 +192,62 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
                 assert "import synth" not in text and "from synth" not in text, f
+
+
+def test_patch_embed_head_and_forward_validation(N):
+    lib = N.lib()
+    E_ARG, E_UNS = N.RS_ERR_INVALID_ARG, N.RS_ERR_UNSUPPORTED
+    d = _desc(N)
+    emb = N.EmbedWeights(FAKE, FAKE, FAKE, FAKE)
+
+    def pe(img, e=emb, desc=d, B=2, images=FAKE, tokens=FAKE):
+        return lib.rs_patch_embed(ctypes.byref(desc), ctypes.byref(img) if img is not None else None,
+                                  ctypes.byref(e), images, B, tokens, None)
+
+    good = N.ImageDesc(1, 3, 224, 224, 16)
+    assert pe(None) == E_ARG
+    assert pe(N.ImageDesc(1, 3, 224, 224, 12)) == E_UNS                 # patch not 8/16/32
+    assert pe(N.ImageDesc(1, 3, 224, 200, 16)) == E_ARG                 # width % patch
+    assert pe(N.ImageDesc(0, 3, 224, 224, 16)) == E_ARG
+    assert pe(N.ImageDesc(1, 0, 224, 224, 16)) == E_ARG
+    assert pe(N.ImageDesc(1000, 3, 224, 224, 16)) == E_UNS              # > RS_MAX_TOKENS
+    assert pe(good, e=N.EmbedWeights(FAKE, FAKE, None, FAKE)) == E_ARG  # class token missing
+    assert pe(good, B=0) == E_ARG
+    assert pe(good, images=None) == E_ARG
+    assert pe(good, tokens=FAKE + 8) == E_ARG
+    assert pe(good, desc=_desc(N, op=5)) == E_ARG
+    nocls = _desc(N, has_cls=0)
+    hw = N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 1000, N.RS_POOL_CLS)
+
+    def hd(h, desc=d, B=2, L=68, x=FAKE, f=FAKE, lg=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.rs_head(ctypes.byref(desc), ctypes.byref(h), x, B, L, f, lg, ws, ws_bytes, None)
+
+    assert hd(N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 1001, N.RS_POOL_CLS)) == E_UNS   # n_out % 8
+    assert hd(N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 0, N.RS_POOL_CLS)) == E_UNS
+    assert hd(N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 1000, 2)) == E_ARG               # pool
+    assert hd(hw, desc=nocls) == E_ARG                                               # no class token
+    assert hd(N.HeadWeights(FAKE, None, FAKE, FAKE, 1000, N.RS_POOL_CLS)) == E_ARG
+    assert hd(hw, f=None) == E_ARG
+    assert hd(hw, L=0) == E_ARG
+    assert hd(hw, ws=FAKE + 64) == E_ARG                                             # alignment
+    need = lib.rs_head_workspace_bytes(2, 68, 384)
+    assert need == 3 * 2 * 384 * 4 and lib.rs_head_workspace_bytes(2, 68, 100) == 0  # 3 row blocks
+    assert hd(hw, ws_bytes=need - 1) == N.RS_ERR_WORKSPACE
+    # whole forward: workspace query and checks before anything is enqueued
+    n1 = lib.rs_vit_workspace_bytes(ctypes.byref(d), ctypes.byref(good), 12, 256)
+    assert n1 > 0
+    assert lib.rs_vit_workspace_bytes(ctypes.byref(d), ctypes.byref(N.ImageDesc(1, 3, 224, 224, 12)), 12, 256) == 0
+    enc_ws = lib.rs_workspace_bytes(ctypes.byref(d), 12, 256, 197)
+    assert n1 > enc_ws + 2 * 256 * 197 * 384 * 2                          # tokens + encoder output
+    blocks = (N.BlockWeights * 12)(*[_weights(N) for _ in range(12)])
+    pl, kr = N.int_array([3, 6, 9]), N.dbl_array([0.7] * 3)
+
+    def fw(ws_bytes=n1, img=good, h=hw, sched=(pl, kr, 3)):
+        return lib.rs_vit_forward(ctypes.byref(d), ctypes.byref(img), ctypes.byref(emb), blocks, 12,
+                                  ctypes.byref(h), FAKE, 256, sched[0], sched[1], sched[2], FAKE,
+                                  FAKE, None, FAKE, ws_bytes, None)
+
+    assert fw(ws_bytes=n1 // 2) == N.RS_ERR_WORKSPACE
+    assert fw(sched=(N.int_array([3, 3]), N.dbl_array([0.7, 0.7]), 2)) == E_ARG
+    assert fw(h=N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 12, N.RS_POOL_CLS)) == E_UNS
+    assert fw(img=N.ImageDesc(1, 3, 224, 224, 12)) == E_UNS

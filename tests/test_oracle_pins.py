@@ -336,3 +336,93 @@ def test_synth_bf16_rounding():
     np.testing.assert_array_equal(r[:3], np.array([1.0, 1.0, 1.0078125], np.float32))
     assert r[3] == np.float32(-2.0)
     assert (r.view(np.uint32) & 0xFFFF).max() == 0
+
+
+# ----------------------------------------------------------------------------- around the encoder
+
+def test_patch_embed_is_a_stride_p_convolution():
+    """Sec. 3.1 tokenisation: the oracle's patch embedding equals a P x P, stride-P
+    convolution (torch's conv2d in float64, a library routine) flattened in raster order,
+    frame after frame, with the class token first and the position table added."""
+    import torch
+    rng = np.random.default_rng(3)
+    T, cin, H, W, P, C = 2, 3, 32, 48, 16, 24
+    img = rng.standard_normal((T, cin, H, W))
+    w = rng.standard_normal((C, cin * P * P))
+    b = rng.standard_normal(C)
+    cls = rng.standard_normal(C)
+    N = T * (H // P) * (W // P)
+    pos = rng.standard_normal((N + 1, C))
+    got = O.patch_embed(img, w, b, cls, pos, P)
+    conv = torch.nn.functional.conv2d(torch.from_numpy(img), torch.from_numpy(w.reshape(C, cin, P, P)),
+                                      torch.from_numpy(b), stride=P)          # [T][C][H/P][W/P]
+    want = conv.flatten(2).transpose(1, 2).reshape(N, C).numpy()
+    np.testing.assert_allclose(got[0], cls + pos[0], rtol=0, atol=0)
+    np.testing.assert_allclose(got[1:], want + pos[1:], rtol=1e-12, atol=1e-12)
+    # without a class token the table covers the patches only
+    got2 = O.patch_embed(img, w, b, None, pos[1:], P)
+    np.testing.assert_allclose(got2, want + pos[1:], rtol=1e-12, atol=1e-12)
+
+
+def test_patch_embed_one_hot_pixel():
+    """A one-hot weight row picks pixel (channel 1, row 2, column 5) of every patch: token
+    i = pr * (W/P) + pc of frame t holds images[t, 1, pr*P + 2, pc*P + 5]."""
+    T, cin, H, W, P = 2, 3, 16, 24, 8
+    img = np.arange(T * cin * H * W, dtype=np.float64).reshape(T, cin, H, W)
+    w = np.zeros((2, cin * P * P))
+    w[1, 1 * P * P + 2 * P + 5] = 1.0
+    toks = O.patch_embed(img, w, np.zeros(2), None, np.zeros((T * (H // P) * (W // P), 2)), P)
+    gw = W // P
+    for t in range(T):
+        for pr in range(H // P):
+            for pc in range(gw):
+                i = t * (H // P) * gw + pr * gw + pc
+                assert toks[i, 1] == img[t, 1, pr * P + 2, pc * P + 5]
+                assert toks[i, 0] == 0.0
+
+
+def test_head_pooling_closed_forms():
+    """Class-token pooling normalises row 0 only; mean pooling averages the normalised
+    rows (not the normalisation of the mean row: the two differ when rows differ in
+    scale); a one-hot head reads single features."""
+    eps = 1e-6
+    C = 4
+    g, bt = np.ones(C), np.zeros(C)
+    x = np.array([[1.0, -1.0, 0.0, 0.0], [0.0, 0.0, 10.0, -10.0]])
+    r = 1.0 / np.sqrt(0.5 + eps)                       # rstd of [1, -1, 0, 0]
+    r2 = 1.0 / np.sqrt(50.0 + eps)                     # rstd of [0, 0, 10, -10]
+    w = np.eye(C)[[2, 0]]                              # logits = (f[2], f[0]) + b
+    hb = np.array([0.5, -0.25])
+    f, lg = O.head(x, g, bt, w, hb, "cls", eps)
+    np.testing.assert_allclose(f, [r, -r, 0.0, 0.0], rtol=1e-14)
+    np.testing.assert_allclose(lg, [0.5, r - 0.25], rtol=1e-14)
+    f, lg = O.head(x, g, bt, w, hb, "mean", eps)
+    np.testing.assert_allclose(f, [r / 2, -r / 2, 5 * r2, -5 * r2], rtol=1e-14)
+    assert abs(f[2] - f[0]) < 1e-5                     # both rows normalise to the same scale
+    np.testing.assert_allclose(lg, [5 * r2 + 0.5, r / 2 - 0.25], rtol=1e-14)
+    # affine LN parameters apply per channel after normalisation
+    f, _ = O.head(x, np.array([2.0, 1.0, 1.0, 1.0]), np.array([0.0, 0.0, 3.0, 0.0]), w, hb, "cls", eps)
+    np.testing.assert_allclose(f, [2 * r, -r, 3.0, 0.0], rtol=1e-14)
+
+
+def test_vit_forward_with_identity_blocks():
+    """Identity blocks (zero residual branches) leave the class token's row at cls +
+    pos[0], so the features are LN(cls + pos[0]); the kept ids are the top tokens by
+    the norm of their embedding."""
+    wl = synth.Workload("t", 1, 9, 64, 1, 256, 3, "f32", True, (0, 2), (0.7, 0.8), "x")
+    rng = np.random.default_rng(5)
+    P, H, W = 8, 16, 32
+    img = rng.standard_normal((1, 3, H, W))
+    emb = {"w_patch": rng.standard_normal((64, 3 * P * P)) * 0.05, "b_patch": np.zeros(64),
+           "cls": np.tile([1.0, -1.0], 32), "pos": np.zeros((9, 64))}
+    zero = ("w_proj", "b_proj", "w_fc2", "b_fc2")
+    blocks = [synth.make_block_weights(wl, b, 5, init="full", zero=zero) for b in range(wl.depth)]
+    hd = {"ln_g": np.ones(64), "ln_b": np.zeros(64), "w_head": np.eye(64)[:8], "b_head": np.zeros(8)}
+    feat, logits, ids = O.vit_forward(img, emb, blocks, hd, 1, P, wl.prune_layers, wl.keep_ratios,
+                                      True, "cls")
+    np.testing.assert_allclose(feat, np.tile([1.0, -1.0], 32) / np.sqrt(1 + 1e-6), rtol=1e-12)
+    np.testing.assert_allclose(logits, feat[:8], rtol=0, atol=0)
+    toks = O.patch_embed(img, emb["w_patch"], emb["b_patch"], emb["cls"], emb["pos"], P)
+    k1 = O.keep_count(0.7, 9)
+    k2 = O.keep_count(0.8, k1)
+    assert ids.tolist() == O.select_kept(np.linalg.norm(toks, axis=1), k2, True)

@@ -16,7 +16,7 @@ from ._native import BLOCK_FIELDS, KERNELS, RSError, lib  # noqa: F401
 
 __all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forward",
            "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib",
-           "set_max_lanes"]
+           "set_max_lanes", "ImageSpec", "patch_embed", "head", "ViT", "vit_forward"]
 
 _DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
 # representation shift variants of the ablations (rs_shift_op, rs_dist of include/rs.h)
@@ -199,6 +199,127 @@ def encoder_forward(spec: ModelSpec, blocks: List[Dict[str, torch.Tensor]], x: t
     enc = Encoder(spec, blocks, B, L, prune_layers, keep_ratios, device=x.device)
     out, idx = enc.forward(x)
     return out, idx
+
+
+class ImageSpec:
+    """Pixel input geometry: frames (1 for an image), channels, height, width, patch size
+    P (8, 16 or 32).  Tokens per sample: has_cls + frames * (height/P) * (width/P)."""
+
+    def __init__(self, frames: int = 1, in_chans: int = 3, height: int = 224, width: int = 224,
+                 patch: int = 16):
+        self.frames, self.in_chans, self.height, self.width, self.patch = (
+            int(frames), int(in_chans), int(height), int(width), int(patch))
+
+    def desc(self) -> N.ImageDesc:
+        return N.ImageDesc(self.frames, self.in_chans, self.height, self.width, self.patch)
+
+    def tokens(self, has_cls: bool) -> int:
+        P = self.patch
+        return int(has_cls) + self.frames * (self.height // P) * (self.width // P)
+
+    def image_shape(self, B: int):
+        return (B, self.frames, self.in_chans, self.height, self.width)
+
+
+def _embed(spec: ModelSpec, img: ImageSpec, e: Dict[str, torch.Tensor]) -> N.EmbedWeights:
+    C, L = spec.C, img.tokens(spec.has_cls)
+    shapes = {"w_patch": (C, img.in_chans * img.patch ** 2), "b_patch": (C,), "cls": (C,),
+              "pos": (L, C)}
+    ptrs = []
+    for n in N.EMBED_FIELDS:
+        if n == "cls" and not spec.has_cls:
+            ptrs.append(None)
+        else:
+            ptrs.append(_dev(e[n], n, spec.dtype, shapes[n]))
+    return N.EmbedWeights(*ptrs)
+
+
+def _head(spec: ModelSpec, h: Dict[str, torch.Tensor], pool: str) -> N.HeadWeights:
+    if pool not in ("cls", "mean"):
+        raise ValueError(f"pool must be 'cls' or 'mean', got {pool!r}")
+    n_out = h["w_head"].shape[0]
+    shapes = {"ln_g": (spec.C,), "ln_b": (spec.C,), "w_head": (n_out, spec.C), "b_head": (n_out,)}
+    ptrs = [_dev(h[n], n, spec.dtype, shapes[n]) for n in N.HEAD_FIELDS]
+    return N.HeadWeights(*ptrs, n_out, N.RS_POOL_CLS if pool == "cls" else N.RS_POOL_MEAN)
+
+
+def patch_embed(spec: ModelSpec, img: ImageSpec, emb: Dict[str, torch.Tensor],
+                images: torch.Tensor) -> torch.Tensor:
+    """Patch embedding: images [B, frames, in_chans, H, W] -> tokens [B, L, C]."""
+    B = images.shape[0]
+    _dev(images, "images", spec.dtype, img.image_shape(B))
+    tokens = torch.empty(B, img.tokens(spec.has_cls), spec.C, dtype=spec.dtype, device=images.device)
+    d, idesc, e = spec.desc(), img.desc(), _embed(spec, img, emb)
+    N.check("rs_patch_embed", lib().rs_patch_embed(ctypes.byref(d), ctypes.byref(idesc),
+                                                   ctypes.byref(e), images.data_ptr(), B,
+                                                   tokens.data_ptr(), _stream()))
+    return tokens
+
+
+def head(spec: ModelSpec, hw: Dict[str, torch.Tensor], x: torch.Tensor, pool: str):
+    """Final LayerNorm, pooling ('cls' or 'mean') and head of x [B, L, C].  Returns
+    (features [B, C], logits [B, n_out])."""
+    B, L, C = x.shape
+    _dev(x, "x", spec.dtype, (B, L, spec.C))
+    h = _head(spec, hw, pool)
+    feat = torch.empty(B, spec.C, dtype=spec.dtype, device=x.device)
+    logits = torch.empty(B, h.n_out, dtype=spec.dtype, device=x.device)
+    ws = torch.empty(int(lib().rs_head_workspace_bytes(B, L, spec.C)), dtype=torch.uint8,
+                     device=x.device)
+    d = spec.desc()
+    N.check("rs_head", lib().rs_head(ctypes.byref(d), ctypes.byref(h), x.data_ptr(), B, L,
+                                     feat.data_ptr(), logits.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream()))
+    return feat, logits
+
+
+class ViT:
+    """The whole forward pass (patch embedding, pruned encoder, head) bound to a batch
+    size, with its workspace and outputs allocated once."""
+
+    def __init__(self, spec: ModelSpec, img: ImageSpec, emb: Dict[str, torch.Tensor],
+                 blocks: List[Dict[str, torch.Tensor]], hw: Dict[str, torch.Tensor], pool: str,
+                 B: int, prune_layers: Sequence[int], keep_ratios: Sequence[float],
+                 device="cuda"):
+        self.spec, self.img, self.B = spec, img, B
+        self.depth = len(blocks)
+        self.L = img.tokens(spec.has_cls)
+        self.prune = list(prune_layers)
+        self.ratios = [float(r) for r in keep_ratios]
+        self.L_final = encoder_out_len(self.depth, self.L, self.prune, self.ratios)
+        self._keep = (emb, blocks, hw)  # keep the tensors alive
+        self._desc, self._idesc = spec.desc(), img.desc()
+        self._emb = _embed(spec, img, emb)
+        self._w = (N.BlockWeights * self.depth)(*[_weights(spec, w) for w in blocks])
+        self._head = _head(spec, hw, pool)
+        self._pl, self._kr = N.int_array(self.prune), N.dbl_array(self.ratios)
+        n = lib().rs_vit_workspace_bytes(ctypes.byref(self._desc), ctypes.byref(self._idesc),
+                                         self.depth, B)
+        if n == 0:
+            raise ValueError("invalid model or image description for the workspace query")
+        self.workspace = torch.empty(int(n), dtype=torch.uint8, device=device)
+        self.features = torch.empty(B, spec.C, dtype=spec.dtype, device=device)
+        self.logits = torch.empty(B, self._head.n_out, dtype=spec.dtype, device=device)
+        self.out_idx = torch.empty(B, self.L_final, dtype=torch.int32, device=device)
+
+    def forward(self, images: torch.Tensor):
+        _dev(images, "images", self.spec.dtype, self.img.image_shape(self.B))
+        N.check("rs_vit_forward", lib().rs_vit_forward(
+            ctypes.byref(self._desc), ctypes.byref(self._idesc), ctypes.byref(self._emb), self._w,
+            self.depth, ctypes.byref(self._head), images.data_ptr(), self.B, self._pl, self._kr,
+            len(self.prune), self.features.data_ptr(), self.logits.data_ptr(),
+            self.out_idx.data_ptr(), self.workspace.data_ptr(), self.workspace.numel(),
+            _stream()))
+        return self.features, self.logits, self.out_idx
+
+
+def vit_forward(spec: ModelSpec, img: ImageSpec, emb, blocks, hw, pool: str,
+                images: torch.Tensor, prune_layers: Sequence[int], keep_ratios: Sequence[float]):
+    """Whole forward pass.  Returns (features [B, C], logits [B, n_out], out_idx
+    [B, L_final])."""
+    m = ViT(spec, img, emb, blocks, hw, pool, images.shape[0], prune_layers, keep_ratios,
+            device=images.device)
+    return m.forward(images)
 
 
 def set_max_lanes(lanes: int) -> None:

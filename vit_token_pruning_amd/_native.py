@@ -13,8 +13,13 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rs.h")
 
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
-KERNELS = ("ln_prep", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score")
+KERNELS = ("ln_prep", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score",
+           "patch_embed", "head")
+RS_POOL_CLS, RS_POOL_MEAN = 0, 1
 
+# field order of rs_embed_weights and of the pointer fields of rs_head_weights
+EMBED_FIELDS = ("w_patch", "b_patch", "cls", "pos")
+HEAD_FIELDS = ("ln_g", "ln_b", "w_head", "b_head")
 # field order of rs_block_weights
 BLOCK_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj",
                 "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
@@ -33,6 +38,20 @@ class ModelDesc(ctypes.Structure):
 
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in BLOCK_FIELDS]
+
+
+class ImageDesc(ctypes.Structure):
+    _fields_ = [("frames", c_int), ("in_chans", c_int), ("height", c_int), ("width", c_int),
+                ("patch", c_int)]
+
+
+class EmbedWeights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in EMBED_FIELDS]
+
+
+class HeadWeights(ctypes.Structure):
+    _fields_ = [("ln_g", c_void_p), ("ln_b", c_void_p), ("w_head", c_void_p),
+                ("b_head", c_void_p), ("n_out", c_int), ("pool", c_int)]
 
 
 class RSError(RuntimeError):
@@ -54,6 +73,8 @@ def lib():
                            "`python -m vit_token_pruning_amd.build` (no fallback exists)")
     L = ctypes.CDLL(LIB_PATH)
     P_DESC, P_W = ctypes.POINTER(ModelDesc), ctypes.POINTER(BlockWeights)
+    P_IMG, P_EMB = ctypes.POINTER(ImageDesc), ctypes.POINTER(EmbedWeights)
+    P_HEAD = ctypes.POINTER(HeadWeights)
     sig = {
         "rs_block_forward": (c_int, [P_DESC, P_W, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -65,6 +86,14 @@ def lib():
         "rs_encoder_forward": (c_int, [P_DESC, P_W, c_int, c_void_p, c_int, c_int, P_INT, P_DBL,
                                        c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "rs_encoder_out_len": (c_int, [c_int, c_int, P_INT, P_DBL, c_int, P_INT]),
+        "rs_patch_embed": (c_int, [P_DESC, P_IMG, P_EMB, c_void_p, c_int, c_void_p, c_void_p]),
+        "rs_head": (c_int, [P_DESC, P_HEAD, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                            c_size_t, c_void_p]),
+        "rs_head_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+        "rs_vit_forward": (c_int, [P_DESC, P_IMG, P_EMB, P_W, c_int, P_HEAD, c_void_p, c_int, P_INT,
+                                   P_DBL, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                   c_void_p]),
+        "rs_vit_workspace_bytes": (c_size_t, [P_DESC, P_IMG, c_int, c_int]),
         "rs_workspace_bytes": (c_size_t, [P_DESC, c_int, c_int, c_int]),
         "rs_last_error": (ctypes.c_char_p, []),
         "rs_set_max_lanes": (c_int, [c_int]),

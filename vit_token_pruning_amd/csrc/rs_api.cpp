@@ -459,14 +459,21 @@ struct LaneRun {
   void* out;
   int32_t* out_idx;
   hipStream_t st;
+  const float* x_st = nullptr;  // slice partials of x's rows if already computed (nullable)
   // progress
-  const void* cur = nullptr;  // block input; its slice partials are always in ws->blk.st_x
+  const void* cur = nullptr;     // block input
+  const float* cur_st = nullptr; // its slice partials (x_st, then ws->blk.st_x)
   int curL = 0, pi = 0;
   const int32_t* ids = nullptr;  // original ids of the current rows (null = identity)
 
   rs_status begin() {
     cur = x;
     curL = L;
+    if (x_st) {
+      cur_st = x_st;
+      return RS_OK;
+    }
+    cur_st = ws->blk.st_x;
     return run_row_stats(*d, x, ws->blk.st_x, B * L, st);
   }
   rs_status block(int b) {
@@ -477,10 +484,11 @@ struct LaneRun {
     const FoldWs fw = fold_of(*d, *enc, b);
     if (!prune) {
       void* dst = last ? out : ws->act;
-      if ((s = run_block(*d, blocks[b], fw, cur, bw.st_x, B, curL, dst, nullptr,
+      if ((s = run_block(*d, blocks[b], fw, cur, cur_st, B, curL, dst, nullptr,
                          last ? nullptr : bw.st_x, bw, st)) != RS_OK)
         return s;
       cur = dst;
+      cur_st = bw.st_x;
       return RS_OK;
     }
     const int k = (*ks)[pi];
@@ -488,7 +496,7 @@ struct LaneRun {
     int32_t* ids_out = last_prune ? out_idx : ws->ids[pi & 1];
     void* dst = last ? out : ws->act;
     const size_t row_bytes = (size_t)d->C * esize(d->dtype);
-    if ((s = run_block(*d, blocks[b], fw, cur, bw.st_x, B, curL, bw.xhat, bw.part,
+    if ((s = run_block(*d, blocks[b], fw, cur, cur_st, B, curL, bw.xhat, bw.part,
                        last ? nullptr : bw.st_xhat, bw, st)) != RS_OK)
       return s;
     // the kept rows and, unless this is the last block, their LayerNorm statistics
@@ -499,6 +507,7 @@ struct LaneRun {
                         last ? nullptr : bw.st_xhat, last ? nullptr : bw.st_x, stat_bytes)) != RS_OK)
       return s;
     cur = dst;
+    cur_st = bw.st_x;
     ids = ids_out;
     curL = k;
     ++pi;
@@ -516,6 +525,178 @@ struct LaneRun {
     return end();
   }
 };
+
+// The encoder on `x` [B][L][C] (x_st: its rows' slice partials, or null to compute
+// them): LayerNorm folding of every block, then the blocks as one or two lanes.
+rs_status run_encoder(const rs_model_desc& d, const rs_block_weights* blocks, int depth,
+                      const void* x, const float* x_st, int B, int L, const int* prune_layers,
+                      int n_prune, const std::vector<int>& ks, int L_final, void* out,
+                      int32_t* out_idx, EncWs& enc, hipStream_t stream) {
+  rs_status s;
+  const int nlanes = enc.nlanes;
+  if ((s = run_fold(d, blocks, enc, 0, depth, stream)) != RS_OK) return s;
+  const size_t row_bytes = (size_t)d.C * esize(d.dtype);
+  LaneRun run[kMaxLanes];
+  for (int i = 0, b0 = 0; i < nlanes; ++i) {
+    const int Bl = lane_batch(B, nlanes, i);
+    LaneRun& r = run[i];
+    r.d = &d; r.blocks = blocks; r.enc = &enc; r.ws = &enc.lane[i];
+    r.depth = depth; r.B = Bl; r.L = L; r.prune_layers = prune_layers; r.n_prune = n_prune; r.ks = &ks;
+    r.x_st = x_st ? x_st + (size_t)b0 * L * rs::stat_stride(d.C) * 2 : nullptr;
+    r.x = static_cast<const char*>(x) + (size_t)b0 * L * row_bytes;
+    r.out = static_cast<char*>(out) + (size_t)b0 * L_final * row_bytes;
+    r.out_idx = out_idx + (size_t)b0 * L_final;
+    b0 += Bl;
+  }
+  if (nlanes == 1) {
+    run[0].st = stream;
+    return run[0].all();
+  }
+  // fork the second lane off the caller's stream, interleave the lanes' launches block by
+  // block, and join it back
+  std::lock_guard<std::mutex> lk(g_lane_mu);
+  LaneStreams* ls = nullptr;
+  if ((s = lane_streams(&ls)) != RS_OK) return s;
+  run[0].st = stream;
+  run[1].st = ls->s2;
+  RS_HIP(hipEventRecord(ls->fork, stream));
+  RS_HIP(hipStreamWaitEvent(ls->s2, ls->fork, 0));
+  for (int i = 0; i < nlanes; ++i)
+    if ((s = run[i].begin()) != RS_OK) return s;
+  for (int blk = 0; blk < depth; ++blk)
+    for (int i = 0; i < nlanes; ++i)
+      if ((s = run[i].block(blk)) != RS_OK) return s;
+  for (int i = 0; i < nlanes; ++i)
+    if ((s = run[i].end()) != RS_OK) return s;
+  RS_HIP(hipEventRecord(ls->join, ls->s2));
+  RS_HIP(hipStreamWaitEvent(stream, ls->join, 0));
+  return RS_OK;
+}
+
+// ------------------------------------------------------------------ around the encoder
+// Geometry of the pixel input: tokens per sample L, patch rows per frame, log2 of P.
+struct ImageGeom {
+  int L, frame_patches, grid_w, lp, K;
+};
+
+rs_status check_image(const rs_model_desc& d, const rs_image_desc* img, ImageGeom* g) {
+  if (!img) return fail(RS_ERR_INVALID_ARG, "image description is null");
+  if (img->frames < 1 || img->in_chans < 1 || img->height < 1 || img->width < 1)
+    return fail(RS_ERR_INVALID_ARG, "frames, in_chans, height and width must be >= 1");
+  int lp = -1;
+  for (int q = 3; q <= 5; ++q)
+    if (img->patch == (1 << q)) lp = q;
+  if (lp < 0) return fail(RS_ERR_UNSUPPORTED, "patch must be 8, 16 or 32");
+  const int P = img->patch;
+  if (img->height % P || img->width % P)
+    return fail(RS_ERR_INVALID_ARG, "height and width must be multiples of the patch size");
+  const long long fp = (long long)(img->height / P) * (img->width / P);
+  const long long L = (d.has_cls ? 1 : 0) + (long long)img->frames * fp;
+  const long long K = (long long)img->in_chans * P * P;
+  if (L > RS_MAX_TOKENS) return fail(RS_ERR_UNSUPPORTED, "tokens per sample > RS_MAX_TOKENS");
+  if (K > (1 << 20)) return fail(RS_ERR_UNSUPPORTED, "in_chans * patch^2 too large");
+  const long long pix = (long long)img->frames * img->in_chans * img->height * img->width;
+  if (pix >= (1LL << 31)) return fail(RS_ERR_UNSUPPORTED, "pixels per sample must stay below 2^31");
+  g->L = (int)L;
+  g->frame_patches = (int)fp;
+  g->grid_w = img->width / P;
+  g->lp = lp;
+  g->K = (int)K;
+  return RS_OK;
+}
+
+rs_status check_embed(const rs_model_desc& d, const rs_embed_weights* e) {
+  if (!e) return fail(RS_ERR_INVALID_ARG, "embedding weights are null");
+  rs_status s;
+  if ((s = check_ptr(e->w_patch, "w_patch")) != RS_OK) return s;
+  if ((s = check_ptr(e->b_patch, "b_patch")) != RS_OK) return s;
+  if ((s = check_ptr(e->pos, "pos")) != RS_OK) return s;
+  if (d.has_cls && (s = check_ptr(e->cls, "cls")) != RS_OK) return s;
+  return RS_OK;
+}
+
+rs_status check_head(const rs_model_desc& d, const rs_head_weights* h) {
+  if (!h) return fail(RS_ERR_INVALID_ARG, "head weights are null");
+  rs_status s;
+  if ((s = check_ptr(h->ln_g, "ln_g")) != RS_OK) return s;
+  if ((s = check_ptr(h->ln_b, "ln_b")) != RS_OK) return s;
+  if ((s = check_ptr(h->w_head, "w_head")) != RS_OK) return s;
+  if ((s = check_ptr(h->b_head, "b_head")) != RS_OK) return s;
+  if (h->n_out < 8 || h->n_out % 8 != 0) return fail(RS_ERR_UNSUPPORTED, "n_out must be a positive multiple of 8");
+  if (h->pool != RS_POOL_CLS && h->pool != RS_POOL_MEAN) return fail(RS_ERR_INVALID_ARG, "unknown pool");
+  if (h->pool == RS_POOL_CLS && !d.has_cls)
+    return fail(RS_ERR_INVALID_ARG, "class-token pooling needs a class token (desc->has_cls)");
+  return RS_OK;
+}
+
+// Patch embedding of B samples into tokens [B][L][C]; the tokens' slice partials to
+// `stats` (nullable).  The class-token rows count no work in the timing.
+rs_status run_patch(const rs_model_desc& d, const rs_image_desc& img, const ImageGeom& g,
+                    const rs_embed_weights& e, const void* images, int B, void* tokens,
+                    float* stats, float* split_ws, hipStream_t st) {
+  const int C = d.C, Ns = img.frames * g.frame_patches, M = B * Ns;
+  rs::GemmEpiArgs ep;
+  ep.bias = e.b_patch; ep.out = tokens; ep.ldo = C; ep.pos = e.pos;
+  ep.img_h = img.height; ep.img_w = img.width; ep.patch_log2 = g.lp; ep.grid_w = g.grid_w;
+  ep.frame_patches = g.frame_patches; ep.sample_patches = Ns; ep.cls_rows = d.has_cls;
+  ep.stats_out = stats; ep.C = C; ep.split_ws = split_ws;
+  RS_HIP(timed(RS_KERNEL_PATCH, 2.0 * M * (double)C * g.K, st, [&] {
+    return rs::launch_gemm(dtype_of(d), rs::kEpiPatch, images, e.w_patch, M, C, g.K, ep, st);
+  }));
+  if (d.has_cls) {
+    RS_HIP(timed(RS_KERNEL_PATCH, 0.0, st, [&] {
+      return rs::launch_cls_rows(dtype_of(d), e.cls, e.pos, tokens, stats, B, g.L, C, st);
+    }));
+  }
+  return RS_OK;
+}
+
+// Scratch of the head: the pooling's partial sums (room for either pooling).
+size_t head_ws_bytes(int B, int L, int C) {
+  return up256((size_t)rs::pool_parts(L, 1) * B * C * 4);
+}
+
+// Final LayerNorm, pooling and head of x [B][L][C].  The pooling counts no work.
+rs_status run_head(const rs_model_desc& d, const rs_head_weights& h, const void* x, int B, int L,
+                   void* features, void* logits, float* pool_ws, float* split_ws, hipStream_t st) {
+  RS_HIP(timed(RS_KERNEL_HEAD, 0.0, st, [&] {
+    return rs::launch_pool(dtype_of(d), x, h.ln_g, h.ln_b, d.ln_eps, B, L, d.C, (int)h.pool,
+                           pool_ws, features, st);
+  }));
+  rs::GemmEpiArgs ep;
+  ep.bias = h.b_head; ep.out = logits; ep.ldo = h.n_out; ep.split_ws = split_ws;
+  RS_HIP(timed(RS_KERNEL_HEAD, 2.0 * B * (double)h.n_out * d.C, st, [&] {
+    return rs::launch_gemm(dtype_of(d), rs::kEpiBias, features, h.w_head, B, h.n_out, d.C, ep, st);
+  }));
+  return RS_OK;
+}
+
+// Workspace of rs_vit_forward: tokens and their slice partials, the encoder output and
+// its ids (worst case: no pruning), the head's scratch, then the encoder's own workspace.
+struct VitWs {
+  void* tokens;
+  float* stats;
+  void* enc_out;
+  int32_t* idx;
+  float* head;
+  char* enc;
+};
+size_t carve_vit(const rs_model_desc& d, int depth, int nlanes, int B, int L, char* base, VitWs* ws) {
+  const size_t M = (size_t)B * L;
+  const size_t sizes[5] = {M * d.C * esize(d.dtype), M * rs::stat_stride(d.C) * 8,
+                           M * d.C * esize(d.dtype), M * 4, head_ws_bytes(B, L, d.C)};
+  void* p[5];
+  const size_t off = carve_seq(base, sizes, 5, p);
+  if (ws) {
+    ws->tokens = p[0];
+    ws->stats = static_cast<float*>(p[1]);
+    ws->enc_out = p[2];
+    ws->idx = static_cast<int32_t*>(p[3]);
+    ws->head = static_cast<float*>(p[4]);
+    ws->enc = base + off;
+  }
+  return off + carve_encoder(d, depth, nlanes, B, L, nullptr, nullptr);
+}
 
 }  // namespace
 
@@ -643,43 +824,105 @@ rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* 
 
   EncWs enc;
   carve_encoder(*desc, depth, nlanes, B, L, static_cast<char*>(workspace), &enc);
-  if ((s = run_fold(*desc, blocks, enc, 0, depth, stream)) != RS_OK) return s;
+  return run_encoder(*desc, blocks, depth, x, nullptr, B, L, prune_layers, n_prune, ks, L_final,
+                     out, out_idx, enc, stream);
+}
 
-  const size_t row_bytes = (size_t)desc->C * esize(desc->dtype);
-  LaneRun run[kMaxLanes];
-  for (int i = 0, b0 = 0; i < nlanes; ++i) {
-    const int Bl = lane_batch(B, nlanes, i);
-    LaneRun& r = run[i];
-    r.d = desc; r.blocks = blocks; r.enc = &enc; r.ws = &enc.lane[i];
-    r.depth = depth; r.B = Bl; r.L = L; r.prune_layers = prune_layers; r.n_prune = n_prune; r.ks = &ks;
-    r.x = static_cast<const char*>(x) + (size_t)b0 * L * row_bytes;
-    r.out = static_cast<char*>(out) + (size_t)b0 * L_final * row_bytes;
-    r.out_idx = out_idx + (size_t)b0 * L_final;
-    b0 += Bl;
+rs_status rs_patch_embed(const rs_model_desc* desc, const rs_image_desc* img,
+                         const rs_embed_weights* emb, const void* images, int B, void* tokens,
+                         hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  ImageGeom g;
+  if ((s = check_image(*desc, img, &g)) != RS_OK) return s;
+  if ((s = check_embed(*desc, emb)) != RS_OK) return s;
+  if ((s = check_BL(B, g.L, desc->C, g.K > desc->C ? g.K : desc->C)) != RS_OK) return s;
+  if ((s = check_ptr(images, "images")) != RS_OK) return s;
+  if ((s = check_ptr(tokens, "tokens")) != RS_OK) return s;
+  return run_patch(*desc, *img, g, *emb, images, B, tokens, nullptr, nullptr, stream);
+}
+
+rs_status rs_head(const rs_model_desc* desc, const rs_head_weights* head, const void* x, int B,
+                  int L, void* features, void* logits, void* workspace, size_t ws_bytes,
+                  hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  if ((s = check_head(*desc, head)) != RS_OK) return s;
+  if ((s = check_BL(B, L, desc->C, head->n_out > desc->C ? head->n_out : desc->C)) != RS_OK) return s;
+  if ((s = check_ptr(x, "x")) != RS_OK) return s;
+  if ((s = check_ptr(features, "features")) != RS_OK) return s;
+  if ((s = check_ptr(logits, "logits")) != RS_OK) return s;
+  if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+  if (ws_bytes < head_ws_bytes(B, L, desc->C))
+    return fail(RS_ERR_WORKSPACE, "workspace too small: need " +
+                                      std::to_string(head_ws_bytes(B, L, desc->C)) + " bytes");
+  return run_head(*desc, *head, x, B, L, features, logits, static_cast<float*>(workspace),
+                  nullptr, stream);
+}
+
+size_t rs_head_workspace_bytes(int B, int L, int C) {
+  if (B < 1 || L < 1 || L > RS_MAX_TOKENS || C < 64 || C > RS_MAX_WIDTH || C % 64) return 0;
+  return head_ws_bytes(B, L, C);
+}
+
+size_t rs_vit_workspace_bytes(const rs_model_desc* desc, const rs_image_desc* img, int depth,
+                              int B) {
+  std::string saved = g_err;
+  ImageGeom g;
+  if (check_desc(desc) != RS_OK || depth < 1 || B < 1 || check_image(*desc, img, &g) != RS_OK) {
+    g_err = saved;
+    return 0;
   }
-  if (nlanes == 1) {
-    run[0].st = stream;
-    return run[0].all();
-  }
-  // fork the second lane off the caller's stream, interleave the lanes' launches block by
-  // block, and join it back
-  std::lock_guard<std::mutex> lk(g_lane_mu);
-  LaneStreams* ls = nullptr;
-  if ((s = lane_streams(&ls)) != RS_OK) return s;
-  run[0].st = stream;
-  run[1].st = ls->s2;
-  RS_HIP(hipEventRecord(ls->fork, stream));
-  RS_HIP(hipStreamWaitEvent(ls->s2, ls->fork, 0));
-  for (int i = 0; i < nlanes; ++i)
-    if ((s = run[i].begin()) != RS_OK) return s;
-  for (int blk = 0; blk < depth; ++blk)
-    for (int i = 0; i < nlanes; ++i)
-      if ((s = run[i].block(blk)) != RS_OK) return s;
-  for (int i = 0; i < nlanes; ++i)
-    if ((s = run[i].end()) != RS_OK) return s;
-  RS_HIP(hipEventRecord(ls->join, ls->s2));
-  RS_HIP(hipStreamWaitEvent(stream, ls->join, 0));
-  return RS_OK;
+  const size_t two = carve_vit(*desc, depth, workspace_lanes(B), B, g.L, nullptr, nullptr);
+  const size_t one = carve_vit(*desc, depth, 1, B, g.L, nullptr, nullptr);
+  return two > one ? two : one;
+}
+
+rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
+                         const rs_embed_weights* emb, const rs_block_weights* blocks, int depth,
+                         const rs_head_weights* head, const void* images, int B,
+                         const int* prune_layers, const double* keep_ratios, int n_prune,
+                         void* features, void* logits, int32_t* out_idx, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  ImageGeom g;
+  if ((s = check_image(*desc, img, &g)) != RS_OK) return s;
+  if ((s = check_embed(*desc, emb)) != RS_OK) return s;
+  if ((s = check_head(*desc, head)) != RS_OK) return s;
+  if (!blocks) return fail(RS_ERR_INVALID_ARG, "blocks is null");
+  int wide = desc->hidden > 3 * desc->C ? desc->hidden : 3 * desc->C;
+  if (g.K > wide) wide = g.K;
+  if ((s = check_BL(B, g.L, desc->C, wide)) != RS_OK) return s;
+  int L_final = 0;
+  std::vector<int> ks;
+  if ((s = check_schedule(depth, g.L, prune_layers, keep_ratios, n_prune, &L_final, &ks)) != RS_OK)
+    return s;
+  for (int b = 0; b < depth; ++b)
+    if ((s = check_weights(&blocks[b])) != RS_OK)
+      return fail(s, "block " + std::to_string(b) + ": " + g_err);
+  if ((s = check_ptr(images, "images")) != RS_OK) return s;
+  if ((s = check_ptr(features, "features")) != RS_OK) return s;
+  if ((s = check_ptr(logits, "logits")) != RS_OK) return s;
+  if (out_idx && (s = check_ptr(out_idx, "out_idx", 4)) != RS_OK) return s;
+  if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+  const int nlanes = encoder_lanes(B, L_final);
+  const size_t need = carve_vit(*desc, depth, nlanes, B, g.L, nullptr, nullptr);
+  if (ws_bytes < need)
+    return fail(RS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+
+  VitWs vw;
+  carve_vit(*desc, depth, nlanes, B, g.L, static_cast<char*>(workspace), &vw);
+  EncWs enc;
+  carve_encoder(*desc, depth, nlanes, B, g.L, vw.enc, &enc);
+  // The patch and head GEMMs never split over K, as in rs_patch_embed and rs_head (which
+  // have no workspace), so the whole pass equals the chain of those calls bit for bit.
+  if ((s = run_patch(*desc, *img, g, *emb, images, B, vw.tokens, vw.stats, nullptr, stream)) != RS_OK)
+    return s;
+  if ((s = run_encoder(*desc, blocks, depth, vw.tokens, vw.stats, B, g.L, prune_layers, n_prune,
+                       ks, L_final, vw.enc_out, out_idx ? out_idx : vw.idx, enc, stream)) != RS_OK)
+    return s;
+  return run_head(*desc, *head, vw.enc_out, B, L_final, features, logits, vw.head, nullptr, stream);
 }
 
 rs_status rs_set_max_lanes(int lanes) {

@@ -106,6 +106,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   constexpr int NPASS = G::BM / 16;
   constexpr bool kFold = EPI == kEpiQKV || EPI == kEpiGelu;   // LayerNorm folded into A
   constexpr bool kResid = EPI == kEpiProj || EPI == kEpiFc2;
+  constexpr bool kPatch = EPI == kEpiPatch;
   const int tid = threadIdx.x;
   const int er = tid >> 4, sub = tid & 15, ec = sub * 8;       // row pass: 16 threads per row
   const int n = n0 + ec;
@@ -126,13 +127,18 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
         rpart[q] = *reinterpret_cast<const float2*>(ep.stats_in + ((size_t)m * sstride + q) * 2);
     }
   }
-  Frag8<T> px[NPASS], pp[NPASS];           // kResid: x (and p) of each row
-  if (kResid) {
+  Frag8<T> px[NPASS], pp[NPASS];           // kResid: x (and p) of each row; kPatch: pos
+  if (kResid || kPatch) {
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
       const int m = m0 + pass * 16 + er;
       if (m < M && col_ok) {
-        load_frag(px[pass], static_cast<const T*>(ep.x) + (size_t)m * N + n);
+        if (kPatch) {
+          const int prow = m % ep.sample_patches + ep.cls_rows;   // row within the sample
+          load_frag(px[pass], static_cast<const T*>(ep.pos) + (size_t)prow * N + n);
+        } else {
+          load_frag(px[pass], static_cast<const T*>(ep.x) + (size_t)m * N + n);
+        }
         if (EPI == kEpiFc2) load_frag(pp[pass], static_cast<const T*>(ep.p) + (size_t)m * N + n);
       }
     }
@@ -200,6 +206,17 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       }
       continue;
     }
+    if (EPI == kEpiBias) {
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += b8[e];
+        store8f(out + (size_t)m * ep.ldo + n, v);
+      }
+      continue;
+    }
+    // output row: the patch embedding leaves room for each sample's class-token row
+    const size_t orow = kPatch ? (size_t)m + (ep.cls_rows ? m / ep.sample_patches + 1 : 0)
+                               : (size_t)m;
     // kEpiProj / kEpiFc2: the output row in fp32 plus its slice partials, and when scoring
     // the representation-shift partials of this thread's columns: s0 (L2: sum of squared
     // differences, L1: sum of |differences|, cosine: sum a.b), s1 and s2 (cosine: a.a, b.b)
@@ -208,7 +225,11 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     if (ok) {
       float xv[8], pv[8];
       frag_to_f32(px[pass], xv);
-      if (EPI == kEpiProj) {
+      if (kPatch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = round_t<T>(v[e] + b8[e] + xv[e]);   // + pos
+        store8f(out + orow * ep.ldo + n, w);
+      } else if (EPI == kEpiProj) {
         float u[8], pf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -263,11 +284,11 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     }
     sm2 = sum8(sm2);
     if ((sub & 7) == 0 && row_ok && slice < nsl && ep.stats_out) {
-      float* so = ep.stats_out + ((size_t)m * sstride + slice) * 2;
+      float* so = ep.stats_out + (orow * sstride + slice) * 2;
       so[0] = smean;
       so[1] = sm2;
     }
-    if (ep.part) {
+    if (!kPatch && ep.part) {
       s0 = sum8(s0);
       if (ep.dist == 2) {
         s1 = sum8(s1);
@@ -326,17 +347,41 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   // that slot lc holds it (the swizzle is an involution).  fp32 (32-byte chunks) goes
   // through registers.
   constexpr bool kDirect = sizeof(T) == 2;
+  // kEpiPatch: A rows are image patches (im2col in the loader).  A chunk is 8 consecutive
+  // pixels of one patch row (the patch width is a multiple of 8), so it is contiguous in
+  // the image; its address is the patch origin plus an offset that depends on k only.
+  constexpr bool kPatchA = EPI == kEpiPatch;
   const int lc = tid % KC, lr = tid / KC;
   const char* ag[NA];
   const char* wg[NW];
-  int sa[NA], sw[NW];
+  int sa[NA], sw[NW], ak[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int r = lr + i * RSTEP;
     const int c = kDirect ? (lc ^ (r % KC)) : lc;
-    ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + c * CB;
+    if constexpr (kPatchA) {
+      const int m = min(m0 + r, M - 1), lp = ep.patch_log2;
+      const int f = m / ep.frame_patches, q = m - f * ep.frame_patches;
+      const int pr = q / ep.grid_w, pc = q - pr * ep.grid_w;
+      const size_t cin = (size_t)(K >> (2 * lp));
+      ag[i] = reinterpret_cast<const char*>(
+          A + ((f * cin * ep.img_h + ((size_t)pr << lp)) * ep.img_w + ((size_t)pc << lp)));
+      ak[i] = kt0 * KC * 8 + c * 8;    // k of this chunk at stage 0
+    } else {
+      ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + c * CB;
+    }
     sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
   }
+  // byte offset of A chunk i at stage kt (from ag[i])
+  auto aoff = [&](int i, int kt) -> size_t {
+    if constexpr (kPatchA) {
+      const int k = ak[i] + kt * KC * 8, lp = ep.patch_log2, pm = (1 << lp) - 1;
+      const int ch = k >> (2 * lp), py = (k >> lp) & pm, pxl = k & pm;
+      return (((size_t)ch * ep.img_h + py) * ep.img_w + pxl) * sizeof(T);
+    } else {
+      return (size_t)kt * ROWB;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int r = lr + i * RSTEP;
@@ -348,7 +393,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   auto gload = [&](int kt, int slot) {
     const size_t off = (size_t)kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) load_frag(ra[slot][i], ag[i] + off);
+    for (int i = 0; i < NA; ++i) load_frag(ra[slot][i], ag[i] + aoff(i, kt));
 #pragma unroll
     for (int i = 0; i < NW; ++i) load_frag(rw[slot][i], wg[i] + off);
   };
@@ -364,7 +409,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     char* s = smem + buf * STAGE;
     const size_t off = (size_t)kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) load_lds16(ag[i] + off, s + (wave * (64 / KC) + i * RSTEP) * ROWB);
+    for (int i = 0; i < NA; ++i) load_lds16(ag[i] + aoff(i, kt), s + (wave * (64 / KC) + i * RSTEP) * ROWB);
 #pragma unroll
     for (int i = 0; i < NW; ++i) load_lds16(wg[i] + off, s + ABYTES + (wave * (64 / KC) + i * RSTEP) * ROWB);
   };
@@ -538,6 +583,8 @@ hipError_t launch_cfg(Dtype dt, GemmEpilogue epi, const void* A, const void* W, 
     case kEpiProj: return launch_epi<T, G, kEpiProj>(dt, a, w, M, N, K, ep, st);
     case kEpiGelu: return launch_epi<T, G, kEpiGelu>(dt, a, w, M, N, K, ep, st);
     case kEpiFc2: return launch_epi<T, G, kEpiFc2>(dt, a, w, M, N, K, ep, st);
+    case kEpiPatch: return launch_epi<T, G, kEpiPatch>(dt, a, w, M, N, K, ep, st);
+    case kEpiBias: return launch_epi<T, G, kEpiBias>(dt, a, w, M, N, K, ep, st);
   }
   return hipErrorInvalidValue;
 }

@@ -28,7 +28,10 @@ enum GemmEpilogue {
   kEpiQKV = 0,   // LN1 folded; Q|K|V -> qkv [M][3C]
   kEpiProj = 1,  // p = acc + b -> out; x' = x + p -> out2; LN2 slice partials of x' -> stats_out
   kEpiGelu = 2,  // LN2 folded, GELU -> out [M][N]                 (fc1)
-  kEpiFc2 = 3    // y = acc + b2; out = (x + p) + y; score partials; LN1 slice partials of out
+  kEpiFc2 = 3,   // y = acc + b2; out = (x + p) + y; score partials; LN1 slice partials of out
+  kEpiPatch = 4, // patch embedding: A gathered from images; out row = acc + b + pos, placed
+                 // after the sample's class-token row; LN1 slice partials of out
+  kEpiBias = 5   // out = acc + b (the head)
 };
 
 struct GemmEpiArgs {
@@ -59,6 +62,14 @@ struct GemmEpiArgs {
   float* stats_out = nullptr;
   // split-K partial tiles, kSplitWsBytes; null disables splitting
   float* split_ws = nullptr;
+  // kEpiPatch: A is images [frames][K >> 2*patch_log2][img_h][img_w]; GEMM row m is patch
+  // m % frame_patches of frame m / frame_patches (raster order, grid_w patches per row),
+  // its K columns the patch's pixels in (channel, row, column) order.  Output row of m:
+  // m + cls_rows * (m / sample_patches + 1); pos [L][N] is indexed by the row within its
+  // sample.
+  const void* pos = nullptr;
+  int img_h = 0, img_w = 0, patch_log2 = 0, grid_w = 0, frame_patches = 0;
+  int sample_patches = 0, cls_rows = 0;
 };
 
 // Split-K.  A GEMM with fewer output tiles than kSplitBelow leaves CUs idle (each tile
@@ -96,6 +107,19 @@ inline int gemm_splits(Dtype dt, int M, int N, int K) {
 // Y = A W^T (+ epilogue).  A [M][K], W [N][K]; K % 64 == 0 (bf16) / % 32 (f32).
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
                        int K, const GemmEpiArgs& ep, hipStream_t stream);
+
+// Class-token rows of the patch embedding: out[b][0] = cls + pos[0] for b < B (rows of
+// L tokens) and their slice partials stats[b * L].
+hipError_t launch_cls_rows(Dtype dt, const void* cls, const void* pos, void* out, float* stats,
+                           int B, int L, int C, hipStream_t stream);
+
+// Final LayerNorm and pooling of x [B][L][C]: mode 0 the class token's normalised row,
+// mode 1 the mean of all rows' normalised rows; feat [B][C] = gamma * pooled + beta.
+// part: pool_parts(L, mode) * B * C floats of scratch (sums over blocks of kPoolRows rows).
+constexpr int kPoolRows = 32;
+inline int pool_parts(int L, int mode) { return mode == 0 ? 1 : (L + kPoolRows - 1) / kPoolRows; }
+hipError_t launch_pool(Dtype dt, const void* x, const void* gamma, const void* beta, float eps,
+                       int B, int L, int C, int mode, float* part, void* feat, hipStream_t stream);
 
 // Slice partials of every row of x [M][C] -> stats [M][stat_stride(C)] float2.
 hipError_t launch_row_stats(Dtype dt, const void* x, float* stats, int M, int C, hipStream_t stream);

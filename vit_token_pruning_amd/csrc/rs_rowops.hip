@@ -99,6 +99,140 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
   }
 }
 
+// ---------------------------------------------------------------- around the encoder
+// Class-token rows of the patch embedding (Sec. 3.1 tokens, class token first):
+// out[b][0] = cls + pos[0] as stored, and that row's slice partials for the first
+// block's LayerNorm.  One wave per sample, lanes as in row_stats_kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void cls_rows_kernel(const T* __restrict__ cls,
+                                                       const T* __restrict__ pos,
+                                                       T* __restrict__ out,
+                                                       float* __restrict__ stats, int B, int L,
+                                                       int C) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= B) return;  // whole wave
+  const size_t row = (size_t)b * L;
+  const int nch = C >> 3, stride = stat_stride(C);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int ch = lane + it * 64;
+    if (it * 64 >= nch) break;  // uniform
+    float v[8];
+    if (ch < nch) {
+      float a[8], q[8];
+      load8f(cls + ch * 8, a);
+      load8f(pos + ch * 8, q);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = round_t<T>(a[e] + q[e]);
+      store8f(out + row * C + ch * 8, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    float sm = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm += v[e];
+    const float mean = sum8(sm) * (1.0f / 64.0f);
+    float m2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mean;
+      m2 += d * d;
+    }
+    m2 = sum8(m2);
+    if ((ch & 7) == 0 && ch < nch && stats) {
+      float* so = stats + (row * stride + (ch >> 3)) * 2;
+      so[0] = mean;
+      so[1] = m2;
+    }
+  }
+}
+
+// Final LayerNorm and pooling before the head, in two launches.  pool_partial_kernel: one
+// workgroup (4 waves) per (sample, block of kPoolRows rows); a wave normalises each of its
+// rows (mean, then biased variance of the deviations, in fp32) and adds the normalised
+// values to per-lane sums of the lane's 8-element chunks; the four waves' sums are added in
+// a fixed order through LDS and written as the block's partial [C].  mode 0 (class token):
+// row 0 alone, one block.  pool_finish_kernel sums a sample's blocks in order, divides by
+// the row count (mode 1) and applies gamma, beta.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_partial_kernel(const T* __restrict__ x, float eps,
+                                                           int L, int C, int mode,
+                                                           float* __restrict__ part) {
+  __shared__ float wsum[4][RS_MAX_WIDTH];
+  const int b = blockIdx.y, blk = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = C >> 3;
+  const float invC = 1.0f / (float)C;
+  float acc[2][8];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[it][e] = 0.f;
+  const int r0 = blk * kPoolRows, r1 = mode == 0 ? 1 : min(L, r0 + kPoolRows);
+  for (int t = r0 + wave; t < r1; t += 4) {
+    const T* xr = x + ((size_t)b * L + t) * C;
+    float v[2][8];
+    float sm = 0.f;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ch = lane + it * 64;
+      if (ch < nch) {
+        load8f(xr + ch * 8, v[it]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[it][e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm += v[it][e];
+    }
+    const float mean = wave_sum(sm) * invC;
+    float q = 0.f;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      if (lane + it * 64 < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = v[it][e] - mean;
+          q += d * d;
+        }
+      }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * invC + eps);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[it][e] += (v[it][e] - mean) * rstd;
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int ch = lane + it * 64;
+    if (ch < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wsum[wave][ch * 8 + e] = acc[it][e];
+    }
+  }
+  __syncthreads();
+  float* out = part + ((size_t)b * gridDim.x + blk) * C;
+  for (int c = threadIdx.x; c < C; c += 256)
+    out[c] = ((wsum[0][c] + wsum[1][c]) + wsum[2][c]) + wsum[3][c];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_finish_kernel(const float* __restrict__ part,
+                                                          const T* __restrict__ gamma,
+                                                          const T* __restrict__ beta, int L,
+                                                          int C, int mode, int nparts,
+                                                          T* __restrict__ feat) {
+  const int b = blockIdx.x;
+  const float inv = mode == 0 ? 1.0f : 1.0f / (float)L;
+  const float* pb = part + (size_t)b * nparts * C;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    float z = 0.f;
+    for (int q = 0; q < nparts; ++q) z += pb[(size_t)q * C + c];
+    z *= inv;
+    feat[(size_t)b * C + c] = from_f32<T>(fmaf(to_f32(gamma[c]), z, to_f32(beta[c])));
+  }
+}
+
 // ---------------------------------------------------------------- standalone score
 // Distance of one token's two rows from its accumulated sums: L2 sqrt(s0); L1 s0; cosine
 // 1 - s0 / max(sqrt(s1) sqrt(s2), 1e-8) with s0 = a.b, s1 = a.a, s2 = b.b.
@@ -496,6 +630,40 @@ hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStrea
     fold_kernel<bf16><<<grid, 256, 0, stream>>>(fa);
   else
     fold_kernel<float><<<grid, 256, 0, stream>>>(fa);
+  return hipGetLastError();
+}
+
+hipError_t launch_cls_rows(Dtype dt, const void* cls, const void* pos, void* out, float* stats,
+                           int B, int L, int C, hipStream_t stream) {
+  const int grid = (B + 3) / 4;
+  if (dt == kBF16)
+    cls_rows_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(cls),
+                                                    static_cast<const bf16*>(pos),
+                                                    static_cast<bf16*>(out), stats, B, L, C);
+  else
+    cls_rows_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(cls),
+                                                     static_cast<const float*>(pos),
+                                                     static_cast<float*>(out), stats, B, L, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(Dtype dt, const void* x, const void* gamma, const void* beta, float eps,
+                       int B, int L, int C, int mode, float* part, void* feat, hipStream_t stream) {
+  const int np = pool_parts(L, mode);
+  const dim3 grid(np, B);
+  if (dt == kBF16) {
+    pool_partial_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(x), eps, L, C,
+                                                        mode, part);
+    pool_finish_kernel<bf16><<<B, 256, 0, stream>>>(part, static_cast<const bf16*>(gamma),
+                                                    static_cast<const bf16*>(beta), L, C, mode,
+                                                    np, static_cast<bf16*>(feat));
+  } else {
+    pool_partial_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), eps, L, C,
+                                                         mode, part);
+    pool_finish_kernel<float><<<B, 256, 0, stream>>>(part, static_cast<const float*>(gamma),
+                                                     static_cast<const float*>(beta), L, C, mode,
+                                                     np, static_cast<float*>(feat));
+  }
   return hipGetLastError();
 }
 
