@@ -26,6 +26,9 @@ FlashAttention" (arXiv HTML page), in float64 NumPy:
   * Sec. 3.1: an H x W image is cut into N = (H/P)(W/P) patches of P x P pixels, the
     tokens the encoder runs on; the model ends in a final LayerNorm and a linear head
     (the DeiT and UMT models the pages run unchanged).
+  * Sec. 3.1, Eq. (2) and Eq. (3): the attention-map importance scores the pages compare
+    against (comparison baselines, not the method): the class token's attention row, or
+    the mean over all queries of the attention rows.
 
 Readings taken where the pages leave a step open (each also listed in the design
 notes of the repository):
@@ -53,7 +56,11 @@ notes of the repository):
     every token (class token included);
   * head: the final LayerNorm of every token, then the class token's normalised row
     (image models with a class token) or the mean of all tokens' normalised rows
-    (video models), then a Linear with bias.
+    (video models), then a Linear with bias;
+  * attention-map scores with several heads: Eq. (2) / Eq. (3) per head (each head's own
+    map, scaled by 1/sqrt(head_dim) as in the attention itself), averaged over the heads;
+    the map is the one the block's attention forms (after LN1); all N queries count in
+    Eq. (3), the class token's included.
 
 Parity status: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (closed forms, textbook identities, brute force on
@@ -131,6 +138,34 @@ def attention_online(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int = 3
     return num / den
 
 
+def attention_maps(xn: np.ndarray, w_qkv, b_qkv, heads: int) -> np.ndarray:
+    """The attention maps A_h = Softmax(q_h k_h^T / sqrt(d)) of every head, [heads, L, L]
+    (query rows, key columns), heads as in multi_head_attention."""
+    L, C = xn.shape
+    d = C // heads
+    qkv = linear(xn, w_qkv, b_qkv)
+    maps = []
+    for h in range(heads):
+        q = qkv[:, h * d:(h + 1) * d]
+        k = qkv[:, C + h * d:C + (h + 1) * d]
+        maps.append(softmax_rows(q @ k.T / math.sqrt(d)))
+    return np.stack(maps)
+
+
+def attention_map_score(maps: np.ndarray, kind: str) -> np.ndarray:
+    """Token importance from attention maps [heads, L, L] (Sec. 3.1): "cls", Eq. (2), the
+    class token's (query 0's) attention row; "mean", Eq. (3), the mean over the N query
+    rows.  Averaged over heads.  Returns [L]."""
+    maps = np.asarray(maps, F64)
+    if kind == "cls":
+        per_head = maps[:, 0, :]
+    elif kind == "mean":
+        per_head = maps.sum(axis=1) / maps.shape[1]
+    else:
+        raise ValueError(kind)
+    return per_head.mean(axis=0)
+
+
 def multi_head_attention(xn: np.ndarray, w_qkv, b_qkv, heads: int, fused: bool = False) -> np.ndarray:
     """Q|K|V = xn W_qkv^T + b (column blocks of C), split each into `heads` groups of
     d = C/heads consecutive columns, attend per head, concatenate heads. Returns [L, C]."""
@@ -150,13 +185,16 @@ def multi_head_attention(xn: np.ndarray, w_qkv, b_qkv, heads: int, fused: bool =
 
 SHIFT_OPS = ("mlp", "attn", "block")
 DISTANCES = ("l2", "l1", "cos")
+MAP_SCORES = ("map_cls", "map_mean")   # Eq. (2) and Eq. (3): comparison baselines
 
 
 def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], heads: int, eps: float = 1e-6,
                   fused_attention: bool = False, op: str = "mlp",
                   dist: str = "l2") -> Dict[str, np.ndarray]:
     """One pre-LN block on one sample x [L, C], Eqs. (5) and (6), plus the representation
-    shift (Eq. (4)) of the chosen operation and distance (Sec. 3.3; the method: MLP, L2).
+    shift (Eq. (4)) of the chosen operation and distance (Sec. 3.3; the method: MLP, L2),
+    or with op "map_cls" / "map_mean" the attention-map score of Eq. (2) / Eq. (3) from
+    this block's attention (dist ignored).
 
     Returns x_prime (Eq. 5), sa (= SA(LN(x))), mlp (= MLP(LN(x'))), x_hat (Eq. 6) and
     score [L]."""
@@ -168,9 +206,13 @@ def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], heads: int, eps: floa
     xn2 = layer_norm(x_prime, w["ln2_g"], w["ln2_b"], eps)
     mlp = linear(gelu(linear(xn2, w["w_fc1"], w["b_fc1"])), w["w_fc2"], w["b_fc2"])
     x_hat = mlp + x_prime                                               # Eq. (6)
-    # Sec. 3.3 operation choice: (i) attention, (ii) MLP, (iii) the entire block
-    f_x, ref = {"attn": (sa, x), "mlp": (mlp, x_prime), "block": (x_hat, x)}[op]
-    score = representation_shift(f_x, ref, dist)                        # Eq. (4)
+    if op in MAP_SCORES:
+        score = attention_map_score(attention_maps(xn1, w["w_qkv"], w["b_qkv"], heads),
+                                    op[4:])                             # Eq. (2) / (3)
+    else:
+        # Sec. 3.3 operation choice: (i) attention, (ii) MLP, (iii) the entire block
+        f_x, ref = {"attn": (sa, x), "mlp": (mlp, x_prime), "block": (x_hat, x)}[op]
+        score = representation_shift(f_x, ref, dist)                    # Eq. (4)
     return {"x_prime": x_prime, "sa": sa, "mlp": mlp, "x_hat": x_hat, "score": score}
 
 

@@ -426,3 +426,55 @@ def test_vit_forward_with_identity_blocks():
     k1 = O.keep_count(0.7, 9)
     k2 = O.keep_count(0.8, k1)
     assert ids.tolist() == O.select_kept(np.linalg.norm(toks, axis=1), k2, True)
+
+
+# ----------------------------------------------------------------------------- Eq. (2) / Eq. (3)
+
+def test_attention_map_scores_closed_forms():
+    """Eq. (2) and Eq. (3) on maps whose softmax has a closed form: zero queries give
+    uniform rows (every score 1/L); one head with two keys whose logits differ by t has
+    rows (sigma(t), 1 - sigma(t)); each Eq. (3) score vector sums to 1 (mean of rows that
+    each sum to 1); heads are averaged."""
+    L, C, heads = 5, 128, 2
+    xn = np.random.default_rng(0).standard_normal((L, C))
+    w = np.zeros((3 * C, C))
+    w[C:2 * C] = np.random.default_rng(1).standard_normal((C, C))   # keys only: Q = 0
+    maps = O.attention_maps(xn, w, np.zeros(3 * C), heads)
+    assert maps.shape == (heads, L, L)
+    for kind in ("cls", "mean"):
+        np.testing.assert_allclose(O.attention_map_score(maps, kind), np.full(L, 1.0 / L), rtol=1e-14)
+    # hand-built maps: head 0 rows (a, 1-a) with a = sigma(t); head 1 uniform
+    t = 0.7
+    a = 1.0 / (1.0 + math.exp(-t))
+    m = np.array([[[a, 1 - a], [1 - a, a]], [[0.5, 0.5], [0.5, 0.5]]])
+    np.testing.assert_allclose(O.attention_map_score(m, "cls"), [(a + 0.5) / 2, (1 - a + 0.5) / 2], rtol=1e-14)
+    np.testing.assert_allclose(O.attention_map_score(m, "mean"), [0.5, 0.5], rtol=1e-14)
+    # a real map from logits: query 0 attends by exp(q.k / 8); Eq. (3) sums to 1
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((7, 64))
+    wq = rng.standard_normal((192, 64)) * 0.3
+    maps = O.attention_maps(x, wq, np.zeros(192), 1)
+    q, k = x @ wq[:64].T, x @ wq[64:128].T
+    e = np.exp(q[0] @ k.T / 8.0)
+    np.testing.assert_allclose(O.attention_map_score(maps, "cls"), e / e.sum(), rtol=1e-12)
+    mean = O.attention_map_score(maps, "mean")
+    assert abs(mean.sum() - 1.0) < 1e-12
+    np.testing.assert_allclose(mean[3], np.mean([np.exp(q[i] @ k[3] / 8) / np.exp(q[i] @ k.T / 8).sum()
+                                                  for i in range(7)]), rtol=1e-12)
+
+
+def test_block_map_scores_use_the_blocks_own_map():
+    """The block's map score is computed from LN1(x) through W_qkv (the attention the block
+    runs); it does not depend on the projection or the MLP."""
+    wl = synth.Workload("t", 1, 9, 128, 2, 512, 1, "f32", True, (0,), (0.7,), "x")
+    x = synth.make_input(wl, 3)[0]
+    w = synth.make_block_weights(wl, 0, 3, init="full")
+    w2 = dict(w, w_proj=w["w_proj"] * 3.0, w_fc2=w["w_fc1"].T.copy() * 0.0 + 0.01)
+    for op, kind in (("map_cls", "cls"), ("map_mean", "mean")):
+        r = O.block_forward(x, w, wl.heads, op=op)
+        xn = O.layer_norm(x, w["ln1_g"], w["ln1_b"], 1e-6)
+        want = O.attention_map_score(O.attention_maps(xn, w["w_qkv"], w["b_qkv"], wl.heads), kind)
+        np.testing.assert_allclose(r["score"], want, rtol=1e-14)
+        np.testing.assert_allclose(O.block_forward(x, w2, wl.heads, op=op)["score"], want, rtol=1e-14)
+        # the block output is the method's
+        np.testing.assert_array_equal(r["x_hat"], O.block_forward(x, w, wl.heads)["x_hat"])
