@@ -237,6 +237,44 @@ def standalone(wl, steps):
     return out
 
 
+def compare(wl, blocks, x, steps, ours, rs, torch):
+    """Context, not `value`: the pages' Base / Attn / Ours structure (Tables 2, 4, 5) on this
+    GPU, encoder only, same weights and input.  base: no pruning, every attention forms and
+    stores its map (a non-fused attention's output); base_fused: no pruning, fused
+    attention; attn: stored maps and pruning by the attention-map score (Eq. (2) with a
+    class token, else Eq. (3)) on the same schedule; ours: the method (the line's value)."""
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    op = "map_cls" if wl.has_cls else "map_mean"
+    cfgs = {"base": ("mlp", True, (), ()), "base_fused": ("mlp", False, (), ()),
+            "attn": (op, True, wl.prune_layers, wl.keep_ratios)}
+    out = {}
+    n = max(5, min(steps, 20))
+    for name, (sop, amap, pl, kr) in cfgs.items():
+        spec = rs.ModelSpec(wl.C, wl.heads, wl.hidden, dt, wl.has_cls, wl.ln_eps, score_op=sop,
+                            attn_map=amap)
+        enc = rs.Encoder(spec, blocks, wl.B, wl.L, pl, kr)
+        for _ in range(3):
+            enc.forward(x)
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(n):
+            enc.forward(x)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / n
+        out[name] = {"value": round(wl.B / (ms / 1e3), 2), "ms_per_step": round(ms, 4)}
+        del enc
+        torch.cuda.empty_cache()
+    out["ours"] = {"value": round(ours, 2)}
+    out["attn_score"] = op
+    out["ours_vs_attn"] = round(ours / out["attn"]["value"], 3)
+    out["ours_vs_base"] = round(ours / out["base"]["value"], 3)
+    log("comparison (encoder):", out)
+    return out
+
+
 def whole_forward(wl, spec, blocks, steps, rs, torch):
     """Context, not `value`: the whole forward pass (patch embedding, the same pruned
     encoder, final LayerNorm and head) from pixels resident in HBM, as the pages'
@@ -294,6 +332,8 @@ def main():
     ap.add_argument("--kernel", default="fc1", choices=[k for k in ("ln_prep", "qkv", "attention",
                     "proj", "fc1", "fc2_score", "topk", "gather")],
                     help="roofline kernel when --no-breakdown is given")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the Base / Attn / Ours comparison (context)")
     ap.add_argument("--no-whole", action="store_true",
                     help="skip the whole-forward context (patch embedding + encoder + head)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -424,6 +464,8 @@ def main():
         line["pages_context"] = {"value": v, "unit": f"{wl.unit}/s", "source": cite,
                                  "note": "RTX A6000, whole forward pass; not the same work",
                                  "ratio": round(value / v, 2)}
+    if not (args.no_compare or args.no_breakdown):
+        line["comparison"] = compare(wl, blocks, x, args.steps, value, rs, torch)
     if not (args.no_whole or args.no_breakdown):
         line["whole_forward"] = whole_forward(wl, spec, blocks, args.steps, rs, torch)
         if wl.name in PAGES_CONTEXT:

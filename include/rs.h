@@ -54,19 +54,32 @@ typedef enum {
 
 typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
 
-/* Which representation shift scores the tokens (Sec. 3.3, "Operation choice"):
+/* Which score ranks the tokens.  A representation shift (Sec. 3.3, "Operation choice"):
  * D(F(z), z) through the MLP sublayer, F(z) = MLP(LN(z)) at z = x' (the method), through
  * the attention sublayer, F = SA(LN(.)) (after the output projection and its bias) at
- * z = x, or through the whole block, D(x_hat, x). */
-typedef enum { RS_SHIFT_MLP = 0, RS_SHIFT_ATTN = 1, RS_SHIFT_BLOCK = 2 } rs_shift_op;
+ * z = x, or through the whole block, D(x_hat, x).  Or, as the comparison baselines of
+ * Sec. 3.1, the block's attention map averaged over heads: the class token's attention
+ * row (Eq. (2); needs desc->has_cls) or the mean of all queries' attention rows
+ * (Eq. (3)).  The map scores run the pruning blocks' attention with the map-forming
+ * kernel (two passes over the keys); score_dist does not apply to them. */
+typedef enum {
+  RS_SHIFT_MLP = 0,
+  RS_SHIFT_ATTN = 1,
+  RS_SHIFT_BLOCK = 2,
+  RS_MAP_CLS = 3,
+  RS_MAP_MEAN = 4
+} rs_shift_op;
 /* Distance D per token (Sec. 3.3, "Distance metrics"): L2 norm of the difference (the
  * method), L1 norm of the difference, or cosine distance 1 - a.b / max(|a| |b|, 1e-8). */
 typedef enum { RS_DIST_L2 = 0, RS_DIST_L1 = 1, RS_DIST_COS = 2 } rs_dist;
 
 /* Shape of one encoder: width C, heads (head dim C/heads = 64), MLP hidden width,
  * LayerNorm epsilon (biased variance), element type, whether token 0 is a class token
- * that selection always keeps, and the score (operation and distance; 0, 0 = the
- * method's MLP-sublayer L2 shift). */
+ * that selection always keeps, the score (operation and distance; 0, 0 = the method's
+ * MLP-sublayer L2 shift), and attn_map: 0 = attention never stores its map (fused;
+ * blocks scored from the map form it in registers only), 1 = every block's attention
+ * forms its map and stores it to HBM ([B][H][L][L rounded up to 8] in the workspace), as
+ * a non-fused attention does -- the comparison setting of the pages' Base and Attn rows. */
 typedef struct {
   int C;
   int heads;
@@ -76,6 +89,7 @@ typedef struct {
   int has_cls;
   rs_shift_op score_op;
   rs_dist score_dist;
+  int attn_map;
 } rs_model_desc;
 
 /* Weights of one pre-LN block (Sec. 3.3, Eqs. (5) and (6)), all of desc.dtype.
@@ -115,6 +129,20 @@ rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype 
 /* Same with the distance of Sec. 3.3 chosen: scores[r] = D(fx[r,:], x[r,:]). */
 rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
                         rs_dist dist, float* scores, hipStream_t stream);
+
+/* Multi-head attention alone (Sec. 3.1, Eq. (1), heads of 64 consecutive columns, scale
+ * 1/8): qkv [B][L][3C] (Q | K | V, as the block's QKV projection writes them) ->
+ * out [B][L][C].  With map, score_cls and score_mean all null it is the fused kernel
+ * that never forms the map.  Otherwise the map-forming kernel runs and writes what is
+ * asked: map [B][H][L][Lpad] (Lpad = L rounded up to a multiple of 8; row i holds query
+ * i's attention over the keys, padding keys 0), score_cls [B][L] = Eq. (2) averaged over
+ * heads (the class token's row; query 0), score_mean [B][L] = Eq. (3) averaged over
+ * heads.  desc supplies C, heads and dtype.  workspace/ws_bytes >=
+ * rs_attention_workspace_bytes(desc, B, L) (may be 0 / null when no score is asked). */
+rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
+                       void* map, float* score_cls, float* score_mean, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
+size_t rs_attention_workspace_bytes(const rs_model_desc* desc, int B, int L);
 
 /* Per-sample selection and compaction: keep the keep_k highest scores of each sample
  * (ties to the lower index, NaN lowest, token 0 always kept if has_cls), write their
@@ -272,7 +300,8 @@ typedef enum {
   RS_KERNEL_SCORE = 8,
   RS_KERNEL_PATCH = 9,        /* patch-embedding GEMM and class-token rows */
   RS_KERNEL_HEAD = 10,        /* final LayerNorm + pooling, and the head GEMM */
-  RS_KERNEL_COUNT = 11
+  RS_KERNEL_MAP_SCORE = 11,   /* Eq. (2) / Eq. (3) scores from the attention kernel's sums */
+  RS_KERNEL_COUNT = 12
 } rs_kernel_id;
 
 rs_status rs_timing_begin(int kernel_id);

@@ -31,10 +31,10 @@ def to_host(t) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
-def spec_of(wl, op: str = "mlp", dist: str = "l2"):
+def spec_of(wl, op: str = "mlp", dist: str = "l2", attn_map: bool = False):
     import vit_token_pruning_amd as rs
     return rs.ModelSpec(wl.C, wl.heads, wl.hidden, torch_dtype(wl.dtype), wl.has_cls, wl.ln_eps,
-                        score_op=op, score_dist=dist)
+                        score_op=op, score_dist=dist, attn_map=attn_map)
 
 
 def oracle_block(x: np.ndarray, w, heads: int, eps: float, samples=None, op: str = "mlp",

@@ -28,8 +28,8 @@ def test_every_declared_symbol_is_exported(N):
         assert hasattr(N.lib(), n), n
 
 
-def _desc(N, C=384, heads=6, hidden=1536, dtype=1, has_cls=1, eps=1e-6, op=0, dist=0):
-    return N.ModelDesc(C, heads, hidden, eps, dtype, has_cls, op, dist)
+def _desc(N, C=384, heads=6, hidden=1536, dtype=1, has_cls=1, eps=1e-6, op=0, dist=0, amap=0):
+    return N.ModelDesc(C, heads, hidden, eps, dtype, has_cls, op, dist, amap)
 
 
 FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
@@ -60,7 +60,9 @@ def test_block_forward_validation(N):
         (dict(desc=_desc(N, hidden=1000)), E_UNS),
         (dict(desc=_desc(N, eps=0.0)), E_ARG),
         (dict(desc=_desc(N, has_cls=2)), E_ARG),
-        (dict(desc=_desc(N, op=3)), E_ARG),                     # unknown score operation
+        (dict(desc=_desc(N, op=5)), E_ARG),                     # unknown score operation
+        (dict(desc=_desc(N, op=3, has_cls=0)), E_ARG),          # Eq. (2) needs a class token
+        (dict(desc=_desc(N, amap=2)), E_ARG),
         (dict(desc=_desc(N, op=-1)), E_ARG),
         (dict(desc=_desc(N, dist=3)), E_ARG),                   # unknown distance
         (dict(k=0), E_ARG),
@@ -155,6 +157,13 @@ def test_workspace_query(N):
     fold = 3 * 384 * 384 * 2
     assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
     assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
+    # stored attention maps: B * H * L * pad8(L) elements; Eq. (3) column sums per 64 queries
+    m = lib.rs_workspace_bytes(ctypes.byref(_desc(N, amap=1)), 1, 256, 197)
+    assert 256 * 6 * 197 * 200 * 2 <= m - a < 256 * 6 * 197 * 200 * 2 + 4096
+    m = lib.rs_workspace_bytes(ctypes.byref(_desc(N, op=4)), 1, 256, 197)
+    assert 256 * 6 * 4 * 197 * 4 <= m - a < 256 * 6 * 4 * 197 * 4 + 4096
+    m = lib.rs_workspace_bytes(ctypes.byref(_desc(N, op=3)), 1, 256, 197)
+    assert 256 * 6 * 197 * 4 <= m - a < 256 * 6 * 197 * 4 + 4096
     # the cosine distance keeps three partial sums per 64-column slice instead of one
     for op in (0, 1, 2):
         c = _desc(N, op=op, dist=2)

@@ -16,22 +16,24 @@ from ._native import BLOCK_FIELDS, KERNELS, RSError, lib  # noqa: F401
 
 __all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forward",
            "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib",
-           "set_max_lanes", "ImageSpec", "patch_embed", "head", "ViT", "vit_forward"]
+           "set_max_lanes", "ImageSpec", "patch_embed", "head", "ViT", "vit_forward", "attention"]
 
 _DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
-# representation shift variants of the ablations (rs_shift_op, rs_dist of include/rs.h)
-SHIFT_OPS = {"mlp": 0, "attn": 1, "block": 2}
+# representation shift variants of the ablations and the attention-map baselines
+# (rs_shift_op, rs_dist of include/rs.h)
+SHIFT_OPS = {"mlp": 0, "attn": 1, "block": 2, "map_cls": 3, "map_mean": 4}
 DISTANCES = {"l2": 0, "l1": 1, "cos": 2}
 
 
 class ModelSpec:
-    """Width, heads (head dim 64), MLP hidden width, LN eps, dtype, class token flag, and
-    the score: score_op "mlp" (the method), "attn" or "block"; score_dist "l2" (the
-    method), "l1" or "cos"."""
+    """Width, heads (head dim 64), MLP hidden width, LN eps, dtype, class token flag, the
+    score: score_op "mlp" (the method), "attn" or "block" (shifts), "map_cls" / "map_mean"
+    (attention-map baselines, Eq. (2) / (3)); score_dist "l2" (the method), "l1" or "cos";
+    and attn_map: every block's attention stores its map (the non-fused comparison)."""
 
     def __init__(self, C: int, heads: int, hidden: int, dtype: torch.dtype = torch.bfloat16,
                  has_cls: bool = True, ln_eps: float = 1e-6, score_op: str = "mlp",
-                 score_dist: str = "l2"):
+                 score_dist: str = "l2", attn_map: bool = False):
         if dtype not in _DT:
             raise TypeError(f"dtype must be float32 or bfloat16, got {dtype}")
         if score_op not in SHIFT_OPS:
@@ -40,12 +42,12 @@ class ModelSpec:
             raise ValueError(f"score_dist must be one of {sorted(DISTANCES)}, got {score_dist!r}")
         self.C, self.heads, self.hidden, self.dtype = C, heads, hidden, dtype
         self.has_cls, self.ln_eps = bool(has_cls), float(ln_eps)
-        self.score_op, self.score_dist = score_op, score_dist
+        self.score_op, self.score_dist, self.attn_map = score_op, score_dist, bool(attn_map)
 
     def desc(self) -> N.ModelDesc:
         return N.ModelDesc(self.C, self.heads, self.hidden, self.ln_eps, _DT[self.dtype],
                            int(self.has_cls), SHIFT_OPS[self.score_op],
-                           DISTANCES[self.score_dist])
+                           DISTANCES[self.score_dist], int(self.attn_map))
 
     def weight_shapes(self):
         C, Hd = self.C, self.hidden
@@ -132,6 +134,29 @@ def score(fx: torch.Tensor, x: torch.Tensor, dist: str = "l2") -> torch.Tensor:
                                                      _DT[x.dtype], DISTANCES[dist], s.data_ptr(),
                                                      _stream()))
     return s
+
+
+def attention(spec: ModelSpec, qkv: torch.Tensor, want_map: bool = False,
+              want_cls: bool = False, want_mean: bool = False):
+    """Multi-head attention of qkv [B, L, 3C].  Returns (out [B, L, C], map
+    [B, H, L, Lpad] or None, Eq. (2) scores [B, L] or None, Eq. (3) scores [B, L] or None).
+    Without any of the optional outputs the fused kernel runs (no map is formed)."""
+    B, L, C3 = qkv.shape
+    _dev(qkv, "qkv", spec.dtype, (B, L, 3 * spec.C))
+    dev = qkv.device
+    out = torch.empty(B, L, spec.C, dtype=spec.dtype, device=dev)
+    lpad = (L + 7) // 8 * 8
+    amap = torch.empty(B, spec.heads, L, lpad, dtype=spec.dtype, device=dev) if want_map else None
+    sc = torch.empty(B, L, dtype=torch.float32, device=dev) if want_cls else None
+    sm = torch.empty(B, L, dtype=torch.float32, device=dev) if want_mean else None
+    d = spec.desc()
+    nws = int(lib().rs_attention_workspace_bytes(ctypes.byref(d), B, L)) if (want_cls or want_mean) else 0
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    N.check("rs_attention", lib().rs_attention(ctypes.byref(d), qkv.data_ptr(), B, L, out.data_ptr(),
+                                               ptr(amap), ptr(sc), ptr(sm), ws.data_ptr(), nws,
+                                               _stream()))
+    return out, amap, sc, sm
 
 
 def topk_gather(scores: torch.Tensor, x: Optional[torch.Tensor], keep_k: int, has_cls: bool):

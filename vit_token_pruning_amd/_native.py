@@ -14,7 +14,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rs.h")
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
 KERNELS = ("ln_prep", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score",
-           "patch_embed", "head")
+           "patch_embed", "head", "map_score")
 RS_POOL_CLS, RS_POOL_MEAN = 0, 1
 
 # field order of rs_embed_weights and of the pointer fields of rs_head_weights
@@ -33,7 +33,7 @@ P_DBL = ctypes.POINTER(c_double)
 class ModelDesc(ctypes.Structure):
     _fields_ = [("C", c_int), ("heads", c_int), ("hidden", c_int), ("ln_eps", c_float),
                 ("dtype", c_int), ("has_cls", c_int), ("score_op", c_int),
-                ("score_dist", c_int)]
+                ("score_dist", c_int), ("attn_map", c_int)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -86,6 +86,9 @@ def lib():
         "rs_encoder_forward": (c_int, [P_DESC, P_W, c_int, c_void_p, c_int, c_int, P_INT, P_DBL,
                                        c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "rs_encoder_out_len": (c_int, [c_int, c_int, P_INT, P_DBL, c_int, P_INT]),
+        "rs_attention": (c_int, [P_DESC, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+        "rs_attention_workspace_bytes": (c_size_t, [P_DESC, c_int, c_int]),
         "rs_patch_embed": (c_int, [P_DESC, P_IMG, P_EMB, c_void_p, c_int, c_void_p, c_void_p]),
         "rs_head": (c_int, [P_DESC, P_HEAD, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
                             c_size_t, c_void_p]),

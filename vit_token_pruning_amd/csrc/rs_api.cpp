@@ -29,7 +29,12 @@ rs_status fail(rs_status s, const std::string& msg) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t esize(rs_dtype dt) { return dt == RS_BF16 ? 2 : 4; }
-// floats of score partials per token: one per 64-column slice and partial quantity
+bool map_score(const rs_model_desc& d) {
+  return d.score_op == RS_MAP_CLS || d.score_op == RS_MAP_MEAN;
+}
+
+// floats of score partials per token: one per 64-column slice and partial quantity (map
+// scores keep one score per token in the same buffer)
 size_t part_stride(const rs_model_desc& d) {
   return (size_t)rs::score_parts(d.C) * rs::dist_quantities((int)d.score_dist);
 }
@@ -80,8 +85,11 @@ rs_status check_desc(const rs_model_desc* d) {
   if (d->hidden % 64 != 0) return fail(RS_ERR_UNSUPPORTED, "hidden % 64 != 0");
   if (!(d->ln_eps > 0.0f) || !isfinite(d->ln_eps)) return fail(RS_ERR_INVALID_ARG, "ln_eps must be > 0");
   if (d->has_cls != 0 && d->has_cls != 1) return fail(RS_ERR_INVALID_ARG, "has_cls must be 0 or 1");
-  if (d->score_op != RS_SHIFT_MLP && d->score_op != RS_SHIFT_ATTN && d->score_op != RS_SHIFT_BLOCK)
+  if (d->score_op < RS_SHIFT_MLP || d->score_op > RS_MAP_MEAN)
     return fail(RS_ERR_INVALID_ARG, "unknown score_op");
+  if (d->score_op == RS_MAP_CLS && !d->has_cls)
+    return fail(RS_ERR_INVALID_ARG, "the class-token attention score needs a class token");
+  if (d->attn_map != 0 && d->attn_map != 1) return fail(RS_ERR_INVALID_ARG, "attn_map must be 0 or 1");
   if (d->score_dist != RS_DIST_L2 && d->score_dist != RS_DIST_L1 && d->score_dist != RS_DIST_COS)
     return fail(RS_ERR_INVALID_ARG, "unknown score_dist");
   return RS_OK;
@@ -155,6 +163,8 @@ struct BlockWs {
   float* st_xp;   // slice partials of x' rows (LayerNorm 2)
   float* st_xhat; // slice partials of x_hat rows (next block's LayerNorm 1)
   float* split;   // split-K partial tiles (rs::kSplitWsBytes)
+  void* map;      // attention maps [B][H][L][map_pad(L)] (desc.attn_map only)
+  float* mapsum;  // Eq. (2) rows [B][H][L] or Eq. (3) column sums [B][H][nq][L] (map scores)
 };
 struct FoldWs {   // LayerNorm folding of one block: W_qkv diag(gamma1); c, d of QKV and fc1
   void* wq;
@@ -174,7 +184,11 @@ size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
 size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws) {
   const size_t e = esize(d.dtype), M = (size_t)B * L, C = d.C;
   const size_t st = M * rs::stat_stride(d.C) * 8;
-  const size_t sizes[11] = {
+  const size_t H = (size_t)d.heads, nq = ((size_t)L + 63) / 64;
+  const size_t map_bytes = d.attn_map ? (size_t)B * H * L * rs::map_pad(L) * e : 0;
+  const size_t mapsum_bytes = d.score_op == RS_MAP_CLS ? (size_t)B * H * L * 4
+                              : d.score_op == RS_MAP_MEAN ? (size_t)B * H * nq * L * 4 : 0;
+  const size_t sizes[13] = {
       M * 3 * C * e,                                     // qkv: Q | K | V
       M * C * e,                                         // o: attention output
       M * C * e,                                         // p: attention branch (proj out)
@@ -184,15 +198,18 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
       M * part_stride(d) * 4,                            // part: score partials
       st, st, st,                                        // slice partials
       rs::kSplitWsBytes,                                 // split-K partial tiles
+      map_bytes, mapsum_bytes,                           // attention maps, map-score sums
   };
-  void* p[11];
-  const size_t off = carve_seq(base, sizes, 11, p);
+  void* p[13];
+  const size_t off = carve_seq(base, sizes, 13, p);
   if (ws) {
     ws->qkv = p[0]; ws->o = p[1]; ws->p = p[2]; ws->xp = p[3]; ws->h = p[4];
     ws->xhat = p[5]; ws->part = static_cast<float*>(p[6]);
     ws->st_x = static_cast<float*>(p[7]); ws->st_xp = static_cast<float*>(p[8]);
     ws->st_xhat = static_cast<float*>(p[9]);
     ws->split = static_cast<float*>(p[10]);
+    ws->map = p[11];
+    ws->mapsum = static_cast<float*>(p[12]);
   }
   return off;
 }
@@ -355,15 +372,25 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
       return rs::launch_gemm(dt, rs::kEpiQKV, x, fw.wq, M, 3 * C, C, ep, st);
     }));
   }
-  RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
-    return rs::launch_attention(dt, ws.qkv, ws.o, B, L, d.heads, st);
-  }));
+  const bool by_map = part && map_score(d);   // this block is scored from its attention map
+  if (d.attn_map || by_map) {
+    float* cls = by_map && d.score_op == RS_MAP_CLS ? ws.mapsum : nullptr;
+    float* colsum = by_map && d.score_op == RS_MAP_MEAN ? ws.mapsum : nullptr;
+    RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
+      return rs::launch_attention_map(dt, ws.qkv, ws.o, B, L, d.heads,
+                                      d.attn_map ? ws.map : nullptr, rs::map_pad(L), cls, colsum, st);
+    }));
+  } else {
+    RS_HIP(timed(RS_KERNEL_ATTENTION, 4.0 * B * (double)L * L * Cd, st, [&] {
+      return rs::launch_attention(dt, ws.qkv, ws.o, B, L, d.heads, st);
+    }));
+  }
   {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
     ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
     ep.split_ws = ws.split;
-    if (part && d.score_op == RS_SHIFT_ATTN) set_score(ep, d, part);
+    if (part && d.score_op == RS_SHIFT_ATTN) set_score(ep, d, part);   // D(p, x)
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiProj, ws.o, w.w_proj, M, C, C, ep, st);
     }));
@@ -381,11 +408,19 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     rs::GemmEpiArgs ep;
     ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
     ep.x = x; ep.p = ws.p;
-    if (part && d.score_op != RS_SHIFT_ATTN) set_score(ep, d, part);
+    if (part && (d.score_op == RS_SHIFT_MLP || d.score_op == RS_SHIFT_BLOCK)) set_score(ep, d, part);
     ep.stats_out = st_out; ep.C = C;
     ep.split_ws = ws.split;
     RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
+    }));
+  }
+  if (by_map) {
+    // Eq. (2) / Eq. (3) per token into part[0 .. M) (the scores run_select reads)
+    const int mode = d.score_op == RS_MAP_CLS ? 0 : 1;
+    const double rd = mode == 0 ? (double)B * d.heads * L : (double)B * d.heads * ((L + 63) / 64) * L;
+    RS_HIP(timed(RS_KERNEL_MAP_SCORE, rd * 4.0 + Md * 4.0, st, [&] {
+      return rs::launch_map_scores(ws.mapsum, ws.mapsum, B, L, d.heads, mode, part, st);
     }));
   }
   return RS_OK;
@@ -501,7 +536,9 @@ struct LaneRun {
       return s;
     // the kept rows and, unless this is the last block, their LayerNorm statistics
     const size_t stat_bytes = (size_t)rs::stat_stride(d->C) * 8;
-    if ((s = run_select(B, curL, k, d->has_cls, nullptr, bw.part, rs::score_parts(d->C),
+    const bool by_map = map_score(*d);
+    if ((s = run_select(B, curL, k, d->has_cls, by_map ? bw.part : nullptr,
+                        by_map ? nullptr : bw.part, rs::score_parts(d->C),
                         (int)d->score_dist, nullptr,
                         ws->kept, ids, ids_out, bw.xhat, dst, row_bytes, st,
                         last ? nullptr : bw.st_xhat, last ? nullptr : bw.st_x, stat_bytes)) != RS_OK)
@@ -750,7 +787,9 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
   if ((s = run_block(*desc, *w, fold_of(*desc, enc, 0), x, ws.blk.st_x, B, L, xhat, ws.blk.part,
                      nullptr, ws.blk, stream)) != RS_OK)
     return s;
-  return run_select(B, L, keep_k, desc->has_cls, nullptr, ws.blk.part, rs::score_parts(desc->C),
+  const bool by_map = map_score(*desc);
+  return run_select(B, L, keep_k, desc->has_cls, by_map ? ws.blk.part : nullptr,
+                    by_map ? nullptr : ws.blk.part, rs::score_parts(desc->C),
                     (int)desc->score_dist, scores, kept_idx, nullptr, nullptr, xhat, y_kept,
                     (size_t)desc->C * esize(desc->dtype), stream);
 }
@@ -776,6 +815,60 @@ rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_d
     return rs::launch_score_rows(dtype == RS_BF16 ? rs::kBF16 : rs::kF32, fx, x, scores, M, C,
                                  (int)dist, stream);
   }));
+  return RS_OK;
+}
+
+size_t rs_attention_workspace_bytes(const rs_model_desc* desc, int B, int L) {
+  std::string saved = g_err;
+  if (check_desc(desc) != RS_OK || B < 1 || L < 1 || L > RS_MAX_TOKENS) {
+    g_err = saved;
+    return 0;
+  }
+  const size_t bhl = (size_t)B * desc->heads * L;
+  return up256(bhl * 4) + up256(bhl * ((L + 63) / 64) * 4);
+}
+
+rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
+                       void* map, float* score_cls, float* score_mean, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  if ((s = check_BL(B, L, desc->C, 3 * desc->C)) != RS_OK) return s;
+  if ((s = check_ptr(qkv, "qkv")) != RS_OK) return s;
+  if ((s = check_ptr(out, "out")) != RS_OK) return s;
+  if (map && (s = check_ptr(map, "map")) != RS_OK) return s;
+  if (score_cls && (s = check_ptr(score_cls, "score_cls", 4)) != RS_OK) return s;
+  if (score_mean && (s = check_ptr(score_mean, "score_mean", 4)) != RS_OK) return s;
+  const rs::Dtype dt = dtype_of(*desc);
+  const double flop = 4.0 * B * (double)L * L * desc->C;
+  const size_t bhl = (size_t)B * desc->heads * L;
+  if (!map && !score_cls && !score_mean) {
+    RS_HIP(timed(RS_KERNEL_ATTENTION, flop, stream, [&] {
+      return rs::launch_attention(dt, qkv, out, B, L, desc->heads, stream);
+    }));
+    return RS_OK;
+  }
+  float *cls = nullptr, *colsum = nullptr;
+  if (score_cls || score_mean) {
+    if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+    if (ws_bytes < rs_attention_workspace_bytes(desc, B, L))
+      return fail(RS_ERR_WORKSPACE, "workspace too small: need " +
+                                        std::to_string(rs_attention_workspace_bytes(desc, B, L)) + " bytes");
+    if (score_cls) cls = static_cast<float*>(workspace);
+    if (score_mean) colsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + up256(bhl * 4));
+  }
+  RS_HIP(timed(RS_KERNEL_ATTENTION, flop, stream, [&] {
+    return rs::launch_attention_map(dt, qkv, out, B, L, desc->heads, map, rs::map_pad(L), cls,
+                                    colsum, stream);
+  }));
+  if (score_cls)
+    RS_HIP(timed(RS_KERNEL_MAP_SCORE, bhl * 4.0 + B * L * 4.0, stream, [&] {
+      return rs::launch_map_scores(cls, nullptr, B, L, desc->heads, 0, score_cls, stream);
+    }));
+  if (score_mean)
+    RS_HIP(timed(RS_KERNEL_MAP_SCORE, bhl * ((L + 63) / 64) * 4.0 + B * L * 4.0, stream, [&] {
+      return rs::launch_map_scores(nullptr, colsum, B, L, desc->heads, 1, score_mean, stream);
+    }));
   return RS_OK;
 }
 

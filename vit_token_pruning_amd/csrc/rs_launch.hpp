@@ -145,6 +145,19 @@ hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStrea
 hipError_t launch_attention(Dtype dt, const void* qkv, void* out, int B, int L, int H,
                             hipStream_t stream);
 
+// Attention that forms the normalised map (two passes over the keys): out as
+// launch_attention; map [B][H][L][Lpad] (nullable; Lpad % 8 == 0, padding keys 0),
+// cls [B][H][L] query 0's row (nullable), colsum [B][H][ceil(L/64)][L] per 64-query
+// block column sums (nullable).
+hipError_t launch_attention_map(Dtype dt, const void* qkv, void* out, int B, int L, int H,
+                                void* map, int Lpad, float* cls, float* colsum,
+                                hipStream_t stream);
+// scores [B][L]: mode 0 mean over heads of cls; mode 1 mean over heads and queries of the
+// column sums.
+hipError_t launch_map_scores(const float* cls, const float* colsum, int B, int L, int H, int mode,
+                             float* scores, hipStream_t stream);
+inline int map_pad(int L) { return (L + 7) / 8 * 8; }
+
 // scores[r] = D(fx[r], x[r]) over C; dist 0 L2, 1 L1, 2 cosine.
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
                              int dist, hipStream_t stream);
