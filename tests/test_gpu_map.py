@@ -47,7 +47,9 @@ def _oracle_heads(qkv_b, heads):
 
 
 CASES = [("deit_t_block", 2, 197), ("deit_s", 3, 197), ("deit_s", 2, 138), ("deit_s@f32", 2, 65),
-         ("umt_b", 1, 1568), ("deit_s", 2, 1), ("deit_s", 2, 64), ("umt_l@f32", 1, 98)]
+         ("umt_b", 1, 1568), ("deit_s", 2, 1), ("deit_s", 2, 64), ("umt_l@f32", 1, 98),
+         # grids of >= 512 two-group workgroups: the fused kernel runs 32 queries per wave
+         ("deit_s", 96, 197), ("deit_s@f32", 96, 130), ("umt_b", 12, 1568)]
 
 
 @pytest.mark.parametrize("name,B,L", CASES)

@@ -25,7 +25,10 @@
 //    the 8 keys of a fragment one element at a time.
 //  - exp2 with log2(e)/sqrt(d) folded into one FMA per score; the hardware exp2 is used
 //    directly (results below 2^-126 flush to zero, which a softmax over at least one
-//    term equal to 1 cannot notice).
+//    term equal to 1 cannot notice).  The running maximum is only moved when it grows
+//    by more than 2^8 (probabilities stay below 2^8 meanwhile), which skips most
+//    rescales of the output registers; row maxima and sums across the four lane rows
+//    use the gfx950 row-swap instructions.
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
 
@@ -192,11 +195,19 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_rows(mx);
+    // The running maximum moves (and the output and denominator are rescaled) only when
+    // some lane's maximum grew by more than 8 in the exp2 domain: until then the stale
+    // maximum keeps every probability below 2^8, and numerator and denominator share it.
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    const float mb = m_new * scale_log2;
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * scale_log2 > 8.0f)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] *= alpha;
+      m_run = m_new;
+    }
+    const float mb = m_run * scale_log2;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -206,10 +217,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
         s[j][v] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+    l_run += psum;
 
     Frag8<T> pf[2];
     pack_p(pf[0], s[0], s[1]);
@@ -261,9 +269,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     if (kt < nk) step(kt, k0, v0, k1, v1);
   }
 
-  float lt = l_run + __shfl_xor(l_run, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / sum_rows(l_run);
   const int q = q0 + l16;
   if (q < L) {
     T* op = out + (row0 + q) * C + h * 64 + 4 * g;

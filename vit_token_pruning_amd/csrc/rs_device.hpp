@@ -160,6 +160,39 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// Combine the values of lanes i, i ^ 16, i ^ 32, i ^ 48 (the four 16-lane rows) with the
+// gfx950 row swaps, plain VALU ops instead of LDS-routed shuffles.  permlane32_swap(v, v)
+// gives every lane (v[i % 32], v[32 + i % 32]); permlane16_swap(v, v) gives (v of the
+// even row, v of the odd row) of the lane's pair of rows (layout checked on the GPU with
+// an in-bounds probe).  Every lane combines the two in the same order, so all four lanes
+// end with the same bits.
+// (The two results are read with __uint_as_float: a bit_cast of each vector element
+// lets this compiler read the first result twice.)
+__device__ __forceinline__ float max_rows(float v) {
+#if __HIP_DEVICE_COMPILE__
+  const unsigned u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+#else
+  return v;
+#endif
+}
+__device__ __forceinline__ float sum_rows(float v) {
+#if __HIP_DEVICE_COMPILE__
+  const unsigned u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+#else
+  return v;
+#endif
+}
+
 // Exact GELU, z * Phi(z), with the device erf.
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
