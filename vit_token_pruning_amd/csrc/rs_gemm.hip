@@ -57,19 +57,31 @@ template <> __device__ __forceinline__ float gelu_t<float>(float x) { return gel
 
 constexpr int kCS = kGemmTile + 4;  // fp32 row stride of the staged output tile
 
-template <typename T, int WM_, int WN_, int TM_, int TN_, int PF_>
+
+template <typename T, int WM_, int WN_, int TM_, int TN_, int PF_, int KC_, int HALVES_, int NBUF_>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, PF = PF_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
-  static constexpr int KC = sizeof(T) == 2 ? 8 : 4;   // 8-element chunks per row per stage
+  static constexpr int KC = KC_;                       // 8-element chunks per row per stage
   static constexpr int CB = Chunk<T>::bytes;
-  static constexpr int ROWB = KC * CB;                 // 128 bytes per tile row
+  static constexpr int ROWB = KC * CB;                 // bytes per tile row of a stage
+  // chunk c of row r sits at slot c ^ swz(r): with 128-byte rows any 8 consecutive rows'
+  // reads of one chunk fall on distinct banks using r % KC; 64-byte rows pair rows r and
+  // r + 4 (same 64-byte quarter of a 256-byte bank line), so they use (r / 4) % KC
+  static constexpr int SWZ_SHIFT = ROWB == 128 ? 0 : 2;
+  static __device__ __forceinline__ int swz(int r) { return (r >> SWZ_SHIFT) % KC; }
+  // the epilogue stages the output tile in HALVES pieces of BM / HALVES rows
+  static constexpr int HALVES = HALVES_;
+  // LDS stage buffers of the direct (bf16) mainloop: 2 = the next stage loads while this
+  // one computes; 1 = load, wait, compute (other workgroups on the CU hide the wait)
+  static constexpr int NBUF = NBUF_;
   static constexpr int ABYTES = BM * ROWB;
   static constexpr int STAGE = (BM + BN) * ROWB;
   static constexpr int NA = BM * KC / NT, NW = BN * KC / NT;
   static constexpr int RSTEP = NT / KC;
   static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "loader must divide evenly");
+  static_assert(ROWB == 128 || ROWB == 64, "stage rows of 64 or 128 bytes");
 };
 
 // Representation-shift partials of 8 columns, distance `dist` between a and b (Sec. 3.3
@@ -97,13 +109,16 @@ __device__ __forceinline__ void shift_partials(int dist, const float* a, const f
 }
 
 // The epilogue of one 128 x 128 output tile, shared by the direct path and the split-K
-// reduction.  `stage(Cs)` writes the tile's fp32 accumulators to LDS as Cs[m][n], with
-// every LDS byte free when it is called.
+// reduction.  `stage(Cs, h)` writes rows [h BM/HALVES, (h+1) BM/HALVES) of the tile's fp32
+// accumulators to LDS as Cs[m - h BM/HALVES][n]; every LDS byte is free when it is first
+// called.  Staging in two halves halves the epilogue's LDS, so that more workgroups fit
+// on a CU.
 template <typename T, int EPI, class G, class Stage>
 __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep, int M, int N,
                                               int m0, int n0, int nt, Stage&& stage) {
   static_assert(G::BM == 128 && G::BN == 128 && G::NT == 256, "epilogue assumes 128x128, 256 threads");
-  constexpr int NPASS = G::BM / 16;
+  constexpr int NPASS = G::BM / 16, HALVES = G::HALVES, HP = NPASS / HALVES;
+  constexpr int HROWS = G::BM / HALVES;
   constexpr bool kFold = EPI == kEpiQKV || EPI == kEpiGelu;   // LayerNorm folded into A
   constexpr bool kResid = EPI == kEpiProj || EPI == kEpiFc2;
   constexpr bool kPatch = EPI == kEpiPatch;
@@ -156,11 +171,10 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   }
 
   float* Cs = reinterpret_cast<float*>(smem);
-  stage(Cs);
 
   // folded LayerNorm: each tile row's (mean * rstd, rstd), merged once from its slice
   // partials (equal-count merge) and shared through LDS
-  float2* Rs = reinterpret_cast<float2*>(smem + G::BM * kCS * 4);
+  float2* Rs = reinterpret_cast<float2*>(smem + HROWS * kCS * 4);
   if (kFold && tid < G::BM) {
     float mean = 0.f;
 #pragma unroll
@@ -176,7 +190,6 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     const float rstd = 1.0f / sqrtf(m2 / (float)ep.C + ep.eps);
     Rs[tid] = make_float2(mean * rstd, rstd);
   }
-  __syncthreads();
 
   // row pass: 8 consecutive columns per thread; lanes 0-7 / 8-15 of a row cover its two
   // 64-column slices of this tile
@@ -184,13 +197,18 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
   T* out = static_cast<T*>(ep.out);
 #pragma unroll
   for (int pass = 0; pass < NPASS; ++pass) {
-    const int mm = pass * 16 + er, m = m0 + mm;
+    if (pass % HP == 0) {
+      if (pass > 0) __syncthreads();   // the previous half's row passes are done with Cs
+      stage(Cs, pass / HP);
+      __syncthreads();
+    }
+    const int mm = pass * 16 + er, m = m0 + mm, ms = mm - (pass / HP) * HROWS;
     const bool row_ok = m < M;
     const bool ok = col_ok && row_ok;
     float v[8];
     {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(Cs + mm * kCS + ec);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(Cs + mm * kCS + ec + 4);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(Cs + ms * kCS + ec);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(Cs + ms * kCS + ec + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[4 + e] = hi[e]; }
     }
@@ -318,8 +336,9 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
   constexpr int KC = G::KC, CB = G::CB, ROWB = G::ROWB, STAGE = G::STAGE, ABYTES = G::ABYTES;
   constexpr int NA = G::NA, NW = G::NW, RSTEP = G::RSTEP, TM = G::TM, TN = G::TN, PF = G::PF;
   // pipeline stages, or the staged fp32 tile plus one float2 per tile row
-  constexpr int EBYTES = SPLIT ? 0 : G::BM * kCS * 4 + G::BM * 8;
-  constexpr int SMEM = 2 * STAGE > EBYTES ? 2 * STAGE : EBYTES;
+  constexpr int EBYTES = SPLIT ? 0 : (G::BM / G::HALVES) * kCS * 4 + G::BM * 8;
+  constexpr int NBUF = sizeof(T) == 2 ? G::NBUF : 2;
+  constexpr int SMEM = NBUF * STAGE > EBYTES ? NBUF * STAGE : EBYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -358,7 +377,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int r = lr + i * RSTEP;
-    const int c = kDirect ? (lc ^ (r % KC)) : lc;
+    const int c = kDirect ? (lc ^ G::swz(r)) : lc;
     if constexpr (kPatchA) {
       const int m = min(m0 + r, M - 1), lp = ep.patch_log2;
       const int f = m / ep.frame_patches, q = m - f * ep.frame_patches;
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     } else {
       ag[i] = reinterpret_cast<const char*>(A + (size_t)min(m0 + r, M - 1) * K) + (size_t)kt0 * ROWB + c * CB;
     }
-    sa[i] = r * ROWB + ((lc ^ (r % KC)) * CB);
+    sa[i] = r * ROWB + ((lc ^ G::swz(r)) * CB);
   }
   // byte offset of A chunk i at stage kt (from ag[i])
   auto aoff = [&](int i, int kt) -> size_t {
@@ -385,9 +404,9 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int r = lr + i * RSTEP;
-    const int c = kDirect ? (lc ^ (r % KC)) : lc;
+    const int c = kDirect ? (lc ^ G::swz(r)) : lc;
     wg[i] = reinterpret_cast<const char*>(W + (size_t)min(n0 + r, N - 1) * K) + (size_t)kt0 * ROWB + c * CB;
-    sw[i] = ABYTES + r * ROWB + ((lc ^ (r % KC)) * CB);
+    sw[i] = ABYTES + r * ROWB + ((lc ^ G::swz(r)) * CB);
   }
   Frag8<T> ra[PF][NA], rw[PF][NW];
   auto gload = [&](int kt, int slot) {
@@ -430,12 +449,12 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * TM * 16 + i * 16 + l16;
-        load_frag(fa[i], As + r * ROWB + ((c ^ (r % KC)) * CB));
+        load_frag(fa[i], As + r * ROWB + ((c ^ G::swz(r)) * CB));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * TN * 16 + j * 16 + l16;
-        load_frag(fw[j], Ws + r * ROWB + ((c ^ (r % KC)) * CB));
+        load_frag(fw[j], Ws + r * ROWB + ((c ^ G::swz(r)) * CB));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -449,12 +468,22 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
     // Two LDS buffers; the loads of stage kt + 1 are issued right after the barrier that
     // ends stage kt - 1 (whose buffer they overwrite) and land during stage kt's matrix work.
     static_assert(NA + NW > 0 && 64 % KC == 0, "direct loads: whole rows per wave");
-    dload(0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_vmem<0>();          // this wave's part of stage kt is in LDS
-      barrier_nofence();       // ... and every wave's; stage kt - 1's reads are done
-      if (kt + 1 < KT) dload(kt + 1, (kt + 1) & 1);
-      compute(kt & 1);
+    if constexpr (NBUF == 1) {
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt > 0) barrier_nofence();   // every wave's reads of stage kt - 1 are done
+        dload(kt, 0);
+        wait_vmem<0>();                  // this wave's part of stage kt is in LDS
+        barrier_nofence();               // ... and every wave's
+        compute(0);
+      }
+    } else {
+      dload(0, 0);
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_vmem<0>();          // this wave's part of stage kt is in LDS
+        barrier_nofence();       // ... and every wave's; stage kt - 1's reads are done
+        if (kt + 1 < KT) dload(kt + 1, (kt + 1) & 1);
+        compute(kt & 1);
+      }
     }
     __syncthreads();           // LDS is reused by the epilogue
   } else {
@@ -498,13 +527,14 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
       }
     return;
   }
-  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs) {
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, int h) {
+    constexpr int HROWS = G::BM / G::HALVES;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = wm * TM * 16 + i * 16 + l16, n = wn * TN * 16 + j * 16 + 4 * g;
-        *reinterpret_cast<f32x4*>(Cs + m * kCS + n) = acc[j][i];
+        if (m / HROWS == h) *reinterpret_cast<f32x4*>(Cs + (m - h * HROWS) * kCS + n) = acc[j][i];
       }
   });
 }
@@ -514,14 +544,25 @@ __global__ __launch_bounds__(G::NT) void gemm_kernel(const T* __restrict__ A,
 // tile epilogue as the direct path.
 template <typename T, int EPI, class G>
 __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int splits, GemmEpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) char smem[G::BM * kCS * 4 + G::BM * 8];
+  __shared__ __attribute__((aligned(16))) char smem[(G::BM / G::HALVES) * kCS * 4 + G::BM * 8];
   constexpr int NPASS = G::BM / 16;
   const int nM = (M + G::BM - 1) / G::BM, nN = (N + G::BN - 1) / G::BN;
   const int t = xcd_contiguous(blockIdx.x, nM * nN);
   const int mt = t / nN, nt = t - mt * nN;
   const int m0 = mt * G::BM, n0 = nt * G::BN;
-  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs) {
-    const int tid = threadIdx.x, er = tid >> 4, ec = (tid & 15) * 8;
+  f32x4 a[NPASS][2];
+  const int tid = threadIdx.x, er = tid >> 4, ec = (tid & 15) * 8;
+  tile_epilogue<T, EPI, G>(smem, ep, M, N, m0, n0, nt, [&](float* Cs, int h) {
+    constexpr int HP = NPASS / G::HALVES;
+    if (h > 0) {
+#pragma unroll
+      for (int pass = h * HP; pass < (h + 1) * HP; ++pass) {
+        const int mm = (pass - h * HP) * 16 + er;
+        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec) = a[pass][0];
+        *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec + 4) = a[pass][1];
+      }
+      return;
+    }
     // Rows and columns past the matrix edge read a clamped, written element instead of
     // branching, so a split's 16 loads per thread are all in flight together; the
     // epilogue never uses those LDS entries.
@@ -530,7 +571,6 @@ __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int 
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass)
       off[pass] = (size_t)min(m0 + pass * 16 + er, M - 1) * N + ncl;
-    f32x4 a[NPASS][2];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) a[pass][0] = a[pass][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const size_t sstep = (size_t)M * N;
@@ -549,7 +589,7 @@ __global__ __launch_bounds__(G::NT) void splitk_reduce_kernel(int M, int N, int 
       }
     }
 #pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
+    for (int pass = 0; pass < HP; ++pass) {
       const int mm = pass * 16 + er;
       *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec) = a[pass][0];
       *reinterpret_cast<f32x4*>(Cs + mm * kCS + ec + 4) = a[pass][1];
@@ -573,17 +613,49 @@ hipError_t launch_epi(Dtype dt, const T* a, const T* w, int M, int N, int K, con
   return hipGetLastError();
 }
 
+// 64-element stages (128-byte rows), two stage buffers and one-piece epilogue staging:
+// 68 KiB of LDS, two workgroups per CU (proj and fc2, whose residual epilogues hold more
+// registers).  fp32 stages 32 elements (128-byte rows of 32-byte chunks) through registers.
+template <typename T> struct TileMainSel;
+template <> struct TileMainSel<bf16> { using type = Tile<bf16, 2, 2, 4, 4, 1, 8, 1, 2>; };
+template <> struct TileMainSel<float> { using type = Tile<float, 2, 2, 4, 4, 1, 4, 1, 2>; };
+template <typename T> using TileMain = typename TileMainSel<T>::type;
+// QKV, fc1 and the patch embedding (bf16): one stage buffer and the epilogue staged in
+// two halves: about 35 KiB of LDS and under 128 registers, so four workgroups share a CU
+// and the others' matrix work covers one's loads and its (VALU-heavy) folded-LayerNorm /
+// GELU epilogue.  Measured against two buffers at DeiT-S: QKV 8 %, fc1 10-13 % faster;
+// fc2 25 % slower (its registers allow only two workgroups, which then wait on every
+// load).  32-element stages with two buffers (also four workgroups) lost to the doubled
+// barrier count.
+template <typename T> struct TileWideSel { using type = typename TileMainSel<T>::type; };
+template <> struct TileWideSel<bf16> { using type = Tile<bf16, 2, 2, 4, 4, 1, 8, 2, 1>; };
+// ... when the launch has enough tiles for the extra workgroups per CU to matter (smaller
+// launches wait on their single buffer with too few neighbours to cover it; the
+// threshold was swept over 0 / 768 / 1536 on DeiT-S, UMT-B and UMT-L)
+#ifndef RS_WIDE_MIN_TILES
+#define RS_WIDE_MIN_TILES 768
+#endif
+inline bool wide_tiles(int M, int N) {
+  return ((M + 127) / 128) * ((N + 127) / 128) >= RS_WIDE_MIN_TILES;
+}
+
 template <typename T, class G>
 hipError_t launch_cfg(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N, int K,
                       const GemmEpiArgs& ep, hipStream_t st) {
   const T* a = static_cast<const T*>(A);
   const T* w = static_cast<const T*>(W);
   switch (epi) {
-    case kEpiQKV: return launch_epi<T, G, kEpiQKV>(dt, a, w, M, N, K, ep, st);
+    case kEpiQKV:
+      return wide_tiles(M, N) ? launch_epi<T, typename TileWideSel<T>::type, kEpiQKV>(dt, a, w, M, N, K, ep, st)
+                              : launch_epi<T, G, kEpiQKV>(dt, a, w, M, N, K, ep, st);
     case kEpiProj: return launch_epi<T, G, kEpiProj>(dt, a, w, M, N, K, ep, st);
-    case kEpiGelu: return launch_epi<T, G, kEpiGelu>(dt, a, w, M, N, K, ep, st);
+    case kEpiGelu:
+      return wide_tiles(M, N) ? launch_epi<T, typename TileWideSel<T>::type, kEpiGelu>(dt, a, w, M, N, K, ep, st)
+                              : launch_epi<T, G, kEpiGelu>(dt, a, w, M, N, K, ep, st);
     case kEpiFc2: return launch_epi<T, G, kEpiFc2>(dt, a, w, M, N, K, ep, st);
-    case kEpiPatch: return launch_epi<T, G, kEpiPatch>(dt, a, w, M, N, K, ep, st);
+    case kEpiPatch:
+      return wide_tiles(M, N) ? launch_epi<T, typename TileWideSel<T>::type, kEpiPatch>(dt, a, w, M, N, K, ep, st)
+                              : launch_epi<T, G, kEpiPatch>(dt, a, w, M, N, K, ep, st);
     case kEpiBias: return launch_epi<T, G, kEpiBias>(dt, a, w, M, N, K, ep, st);
   }
   return hipErrorInvalidValue;
@@ -591,7 +663,6 @@ hipError_t launch_cfg(Dtype dt, GemmEpilogue epi, const void* A, const void* W, 
 
 // fc2 always runs with 2 waves of 64 columns across a 128-column tile, so the score
 // partial count per row is 2 * ceil(C / 128) (see score_parts()).
-template <typename T> using TileMain = Tile<T, 2, 2, 4, 4, 1>;
 
 }  // namespace
 
