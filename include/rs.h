@@ -162,13 +162,15 @@ rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C
  *  out      [B][L_final][C] encoder output (L_final from rs_encoder_out_len).
  *  out_idx  [B][L_final] original token index of every output row.
  *  workspace/ws_bytes   >= rs_workspace_bytes(desc, depth, B, L).
- * Concurrency: when B >= 2 and each half of the batch still has >= 1024 rows after the
- * last pruning (ceil(B/2) * L_final and floor(B/2) * L_final), the batch runs as two
- * lanes -- samples [0, ceil(B/2)) on `stream`, the rest on a stream the library owns
- * (default priority), forked from and joined back into `stream` with events -- so one
- * lane's memory-bound phases overlap the other's matrix work.  Per-sample results do not
- * depend on the lane split except through a GEMM's split over K, which depends on its
- * row count.  All work is ordered after prior work on `stream` and before later work. */
+ * Concurrency: the batch runs as n lanes, n the largest count up to the process-wide
+ * maximum (rs_set_max_lanes) for which every lane keeps >= 1024 rows after the last
+ * pruning (floor(B/n) * L_final >= 1024) -- lane i takes a contiguous share of the
+ * samples, floor(B/n) or one more (the first B mod n lanes); lane 0 runs on `stream`, the
+ * others on streams the library owns (default priority), forked from and joined back
+ * into `stream` with events -- so one lane's memory-bound phases overlap another's
+ * matrix work.  Per-sample results do not depend on the lane split except through a
+ * GEMM's split over K, which depends on its row count.  All work is ordered after prior
+ * work on `stream` and before later work; the call can be captured into a HIP graph. */
 rs_status rs_encoder_forward(const rs_model_desc* desc, const rs_block_weights* blocks,
                              int depth, const void* x, int B, int L,
                              const int* prune_layers, const double* keep_ratios, int n_prune,
@@ -269,8 +271,9 @@ rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers,
  * invalid description. */
 size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L);
 
-/* Host only: most lanes rs_encoder_forward may use (1 or 2; default 2).  1 keeps every
- * launch on the caller's stream.  Process-wide; affects calls made after it returns. */
+/* Host only: most lanes rs_encoder_forward may use (1 .. 4; default 2).  1 keeps every
+ * launch on the caller's stream.  Process-wide; affects calls made after it returns
+ * (rs_workspace_bytes covers every lane count). */
 rs_status rs_set_max_lanes(int lanes);
 
 /* Message for the calling thread's last failed call ("" if none); valid until the next

@@ -176,9 +176,9 @@ def test_workspace_query(N):
 def test_set_max_lanes(N):
     lib = N.lib()
     assert lib.rs_set_max_lanes(0) == N.RS_ERR_INVALID_ARG
-    assert lib.rs_set_max_lanes(3) == N.RS_ERR_INVALID_ARG
-    assert lib.rs_set_max_lanes(1) == N.RS_OK
-    assert lib.rs_set_max_lanes(2) == N.RS_OK
+    assert lib.rs_set_max_lanes(5) == N.RS_ERR_INVALID_ARG
+    for n in (1, 3, 4, 2):
+        assert lib.rs_set_max_lanes(n) == N.RS_OK
 
 
 def test_timing_session_without_launches(N):

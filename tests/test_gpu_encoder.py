@@ -5,9 +5,10 @@ rs_encoder_forward is checked bit-exactly against chains of rs_block_forward cal
 the same shapes (same kernels, deterministic), whose per-block results are checked
 against the oracle on sampled samples with teacher forcing: the oracle block is fed the
 GPU's own block input, so each comparison measures one block's rounding.  The encoder
-runs a batch as two lanes (the first ceil(B/2) samples and the rest, on two streams)
-when each lane keeps >= 1024 rows after the last pruning; the reference chains run per
-lane, since a GEMM's split over K depends on its row count and so on the lane's batch."""
+runs a batch as n lanes (contiguous shares of the samples on n streams; n up to the
+process-wide maximum, default 2) when every lane keeps >= 1024 rows after the last
+pruning; the reference chains run per lane, since a GEMM's split over K depends on its
+row count and so on the lane's batch."""
 import numpy as np
 import pytest
 
@@ -22,10 +23,16 @@ SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2],
            "deit_s512": [511], "umt_l12f_ret": [13]}
 
 
-def lanes(B, L_final):
-    if B < 2 or (B // 2) * L_final < 1024:
-        return [(0, B)]
-    return [(0, (B + 1) // 2), ((B + 1) // 2, B)]
+def lanes(B, L_final, max_lanes=2):
+    n = max_lanes
+    while n > 1 and (B < n or (B // n) * L_final < 1024):
+        n -= 1
+    out, b0 = [], 0
+    for i in range(n):
+        b1 = b0 + B // n + (1 if i < B % n else 0)
+        out.append((b0, b1))
+        b0 = b1
+    return out
 
 
 def chain_and_check(wl, blocks, wd, xd, samp):
@@ -63,7 +70,7 @@ def chain_and_check(wl, blocks, wd, xd, samp):
     return cur, ids, exact, total
 
 
-def check_encoder(wl, samples):
+def check_encoder(wl, samples, max_lanes=2):
     import torch
     import vit_token_pruning_amd as rs
     spec = spec_of(wl)
@@ -78,7 +85,7 @@ def check_encoder(wl, samples):
     assert tuple(out.shape) == (wl.B, L_final, wl.C)
 
     exact = total = 0
-    for b0, b1 in lanes(wl.B, L_final):
+    for b0, b1 in lanes(wl.B, L_final, max_lanes):
         samp = [s - b0 for s in samples if b0 <= s < b1]
         cur, ids, e, t = chain_and_check(wl, blocks, wd, xd[b0:b1].contiguous(), samp)
         exact, total = exact + e, total + t
@@ -162,3 +169,18 @@ def test_encoder_replays_from_a_hip_graph(B):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(enc.out, ref) and torch.equal(enc.out_idx, ref_idx)
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_encoder_more_lanes(n):
+    """rs_set_max_lanes(3 / 4): 64 samples keeping 68 tokens run as 3 lanes (22, 21, 21
+    samples) or 4 lanes (16 each), each equal to its chain of blocks."""
+    import dataclasses
+    import vit_token_pruning_amd as rs
+    wl = dataclasses.replace(synth.WORKLOADS["deit_s"], B=64, L=97, depth=3, prune_layers=(1,),
+                             keep_ratios=(0.7,))
+    try:
+        rs.set_max_lanes(n)
+        check_encoder(wl, [0, 63], max_lanes=n)
+    finally:
+        rs.set_max_lanes(2)

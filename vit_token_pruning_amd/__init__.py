@@ -348,7 +348,8 @@ def vit_forward(spec: ModelSpec, img: ImageSpec, emb, blocks, hw, pool: str,
 
 
 def set_max_lanes(lanes: int) -> None:
-    """Most concurrent lanes (streams) the encoder may split a batch into: 1 or 2."""
+    """Most concurrent lanes (streams) the encoder may split a batch into: 1 .. 4
+    (default 2)."""
     N.check("rs_set_max_lanes", lib().rs_set_max_lanes(int(lanes)))
 
 

@@ -251,21 +251,26 @@ size_t carve_lane(const rs_model_desc& d, int B, int L, char* base, LaneWs* ws) 
   return off;
 }
 
-// The encoder runs its batch as two lanes on two streams (the first (B + 1) / 2 samples
-// on the caller's stream, the rest on a library stream) when each lane keeps at least
+// The encoder runs its batch as up to g_max_lanes lanes on as many streams (lane 0 on the
+// caller's stream, the others on library streams; lane i takes a contiguous share of
+// the samples, the first B % n lanes one sample more) when every lane keeps at least
 // kLaneMinRows rows after the last pruning, so one lane's memory-bound epilogues and
-// partial last rounds of workgroups overlap the other lane's matrix work.  Smaller lanes
+// partial last rounds of workgroups overlap another lane's matrix work.  Smaller lanes
 // lose more to per-launch latency and extra K splits than the overlap gains (measured:
 // UMT-L at 2 x 98 final rows per lane 6.6 % slower, DeiT-S at 128 x 68 5.9 % faster).
 // rs_block_forward uses one lane.
-constexpr int kMaxLanes = 2;
+constexpr int kMaxLanes = 4;
 constexpr long kLaneMinRows = 1024;
-std::atomic<int> g_max_lanes{2};
+#ifndef RS_DEFAULT_LANES
+#define RS_DEFAULT_LANES 2
+#endif
+std::atomic<int> g_max_lanes{RS_DEFAULT_LANES};
 int encoder_lanes(int B, int L_final) {
-  return g_max_lanes.load() >= 2 && B >= 2 && (long)(B / 2) * L_final >= kLaneMinRows ? 2 : 1;
+  int n = g_max_lanes.load();
+  while (n > 1 && (B < n || (long)(B / n) * L_final < kLaneMinRows)) --n;
+  return n;
 }
-int workspace_lanes(int B) { return B >= 2 ? 2 : 1; }
-int lane_batch(int B, int nlanes, int i) { return nlanes == 1 ? B : (i == 0 ? (B + 1) / 2 : B / 2); }
+int lane_batch(int B, int nlanes, int i) { return B / nlanes + (i < B % nlanes ? 1 : 0); }
 
 struct EncWs {
   int nlanes;
@@ -294,13 +299,13 @@ FoldWs fold_of(const rs_model_desc& d, const EncWs& ws, int b) {
   return fw;
 }
 
-// The second lane's stream and the fork / join events, one set per device, created on
+// The other lanes' streams and the fork / join events, one set per device, created on
 // first use (default priority, non-blocking).  g_lane_mu is held while an encoder call
 // enqueues, so calls from several host threads cannot interleave their event records.
 struct LaneStreams {
   bool ready = false;
-  hipStream_t s2 = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t s[kMaxLanes - 1] = {};
+  hipEvent_t fork = nullptr, join[kMaxLanes - 1] = {};
 };
 std::mutex g_lane_mu;
 std::vector<LaneStreams> g_lanes;
@@ -463,16 +468,18 @@ rs_status run_select(int B, int L, int k, int has_cls, const float* scores, cons
   return RS_OK;
 }
 
-// Second-lane stream and events of the current device (g_lane_mu held by the caller).
+// Lane streams and events of the current device (g_lane_mu held by the caller).
 rs_status lane_streams(LaneStreams** out) {
   int dev = 0;
   RS_HIP(hipGetDevice(&dev));
   if ((int)g_lanes.size() <= dev) g_lanes.resize(dev + 1);
   LaneStreams& l = g_lanes[dev];
   if (!l.ready) {
-    RS_HIP(hipStreamCreateWithFlags(&l.s2, hipStreamNonBlocking));
+    for (int i = 0; i < kMaxLanes - 1; ++i) {
+      RS_HIP(hipStreamCreateWithFlags(&l.s[i], hipStreamNonBlocking));
+      RS_HIP(hipEventCreateWithFlags(&l.join[i], hipEventDisableTiming));
+    }
     RS_HIP(hipEventCreateWithFlags(&l.fork, hipEventDisableTiming));
-    RS_HIP(hipEventCreateWithFlags(&l.join, hipEventDisableTiming));
     l.ready = true;
   }
   *out = &l;
@@ -589,15 +596,17 @@ rs_status run_encoder(const rs_model_desc& d, const rs_block_weights* blocks, in
     run[0].st = stream;
     return run[0].all();
   }
-  // fork the second lane off the caller's stream, interleave the lanes' launches block by
-  // block, and join it back
+  // fork the other lanes off the caller's stream, interleave the lanes' launches block by
+  // block, and join them back
   std::lock_guard<std::mutex> lk(g_lane_mu);
   LaneStreams* ls = nullptr;
   if ((s = lane_streams(&ls)) != RS_OK) return s;
   run[0].st = stream;
-  run[1].st = ls->s2;
   RS_HIP(hipEventRecord(ls->fork, stream));
-  RS_HIP(hipStreamWaitEvent(ls->s2, ls->fork, 0));
+  for (int i = 1; i < nlanes; ++i) {
+    run[i].st = ls->s[i - 1];
+    RS_HIP(hipStreamWaitEvent(ls->s[i - 1], ls->fork, 0));
+  }
   for (int i = 0; i < nlanes; ++i)
     if ((s = run[i].begin()) != RS_OK) return s;
   for (int blk = 0; blk < depth; ++blk)
@@ -605,8 +614,10 @@ rs_status run_encoder(const rs_model_desc& d, const rs_block_weights* blocks, in
       if ((s = run[i].block(blk)) != RS_OK) return s;
   for (int i = 0; i < nlanes; ++i)
     if ((s = run[i].end()) != RS_OK) return s;
-  RS_HIP(hipEventRecord(ls->join, ls->s2));
-  RS_HIP(hipStreamWaitEvent(stream, ls->join, 0));
+  for (int i = 1; i < nlanes; ++i) {
+    RS_HIP(hipEventRecord(ls->join[i - 1], ls->s[i - 1]));
+    RS_HIP(hipStreamWaitEvent(stream, ls->join[i - 1], 0));
+  }
   return RS_OK;
 }
 
@@ -748,9 +759,13 @@ size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L) {
     g_err = saved;
     return 0;
   }
-  const size_t enc = carve_encoder(*desc, depth, workspace_lanes(B), B, L, nullptr, nullptr);
-  const size_t one = carve_encoder(*desc, depth, 1, B, L, nullptr, nullptr);
-  return enc > one ? enc : one;
+  // enough for any lane count the encoder may choose
+  size_t need = 0;
+  for (int n = 1; n <= kMaxLanes && n <= B; ++n) {
+    const size_t w = carve_encoder(*desc, depth, n, B, L, nullptr, nullptr);
+    if (w > need) need = w;
+  }
+  return need;
 }
 
 rs_status rs_encoder_out_len(int depth, int L, const int* prune_layers, const double* keep_ratios,
@@ -966,9 +981,12 @@ size_t rs_vit_workspace_bytes(const rs_model_desc* desc, const rs_image_desc* im
     g_err = saved;
     return 0;
   }
-  const size_t two = carve_vit(*desc, depth, workspace_lanes(B), B, g.L, nullptr, nullptr);
-  const size_t one = carve_vit(*desc, depth, 1, B, g.L, nullptr, nullptr);
-  return two > one ? two : one;
+  size_t need = 0;
+  for (int n = 1; n <= kMaxLanes && n <= B; ++n) {
+    const size_t w = carve_vit(*desc, depth, n, B, g.L, nullptr, nullptr);
+    if (w > need) need = w;
+  }
+  return need;
 }
 
 rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
@@ -1019,7 +1037,7 @@ rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
 }
 
 rs_status rs_set_max_lanes(int lanes) {
-  if (lanes < 1 || lanes > kMaxLanes) return fail(RS_ERR_INVALID_ARG, "lanes must be 1 or 2");
+  if (lanes < 1 || lanes > kMaxLanes) return fail(RS_ERR_INVALID_ARG, "lanes must be 1 .. 4");
   g_max_lanes.store(lanes);
   return RS_OK;
 }

@@ -57,7 +57,6 @@ template <> __device__ __forceinline__ float gelu_t<float>(float x) { return gel
 
 constexpr int kCS = kGemmTile + 4;  // fp32 row stride of the staged output tile
 
-
 template <typename T, int WM_, int WN_, int TM_, int TN_, int PF_, int KC_, int HALVES_, int NBUF_>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, PF = PF_;
@@ -66,11 +65,9 @@ struct Tile {
   static constexpr int KC = KC_;                       // 8-element chunks per row per stage
   static constexpr int CB = Chunk<T>::bytes;
   static constexpr int ROWB = KC * CB;                 // bytes per tile row of a stage
-  // chunk c of row r sits at slot c ^ swz(r): with 128-byte rows any 8 consecutive rows'
-  // reads of one chunk fall on distinct banks using r % KC; 64-byte rows pair rows r and
-  // r + 4 (same 64-byte quarter of a 256-byte bank line), so they use (r / 4) % KC
-  static constexpr int SWZ_SHIFT = ROWB == 128 ? 0 : 2;
-  static __device__ __forceinline__ int swz(int r) { return (r >> SWZ_SHIFT) % KC; }
+  // chunk c of row r sits at slot c ^ swz(r): any 8 consecutive rows' reads of one
+  // chunk then fall on distinct banks
+  static __device__ __forceinline__ int swz(int r) { return r % KC; }
   // the epilogue stages the output tile in HALVES pieces of BM / HALVES rows
   static constexpr int HALVES = HALVES_;
   // LDS stage buffers of the direct (bf16) mainloop: 2 = the next stage loads while this
@@ -81,7 +78,7 @@ struct Tile {
   static constexpr int NA = BM * KC / NT, NW = BN * KC / NT;
   static constexpr int RSTEP = NT / KC;
   static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "loader must divide evenly");
-  static_assert(ROWB == 128 || ROWB == 64, "stage rows of 64 or 128 bytes");
+  static_assert(ROWB == 128, "stage rows of 128 bytes");
 };
 
 // Representation-shift partials of 8 columns, distance `dist` between a and b (Sec. 3.3
