@@ -19,51 +19,15 @@
 // K and V tiles are staged as in the fused kernel (bf16: direct global -> LDS loads into
 // swizzled 128-byte rows, V read with LDS transpose reads; fp32: registers and padded
 // rows).
+#include "rs_attn_frag.hpp"
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
 
 namespace rs {
 namespace {
 
-__device__ __forceinline__ void pack_p(Frag8<bf16>& f, const f32x4& a, const f32x4& b) {
-  f.v[0] = pack_bf16x2(a[0], a[1]);
-  f.v[1] = pack_bf16x2(a[2], a[3]);
-  f.v[2] = pack_bf16x2(b[0], b[1]);
-  f.v[3] = pack_bf16x2(b[2], b[3]);
-}
-__device__ __forceinline__ void pack_p(Frag8<float>& f, const f32x4& a, const f32x4& b) {
-  f.v[0] = __builtin_bit_cast(u32x4, a);
-  f.v[1] = __builtin_bit_cast(u32x4, b);
-}
-__device__ __forceinline__ const char* vt_addr(const char* Vs, int row, int d) {
-  const int c = d >> 3;
-  return Vs + row * 128 + ((c ^ (row & 7)) << 4) + ((d & 7) << 1);
-}
-__device__ __forceinline__ void load_vt(Frag8<bf16>& f, const char* Vs, int kb, int d0, int l16) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const int row = kb + (l16 >> 2), d = d0 + 4 * (l16 & 3);
-  const char* pa = vt_addr(Vs, row, d);
-  const char* pb = vt_addr(Vs, row + 16, d);
-#if __HIP_DEVICE_COMPILE__
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pa));
-  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb));
-#else
-  const v4i16 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-#endif
-  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-  f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
-}
-template <int ROWBV>
-__device__ __forceinline__ void load_vt_f32(Frag8<float>& f, const char* Vs, int kb, int d0, int l16) {
-  float* e = reinterpret_cast<float*>(&f);
-  const char* col = Vs + (d0 + l16) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    e[i] = *reinterpret_cast<const float*>(col + (kb + i) * ROWBV);
-    e[4 + i] = *reinterpret_cast<const float*>(col + (kb + 16 + i) * ROWBV);
-  }
-}
+using namespace attn;
+
 __device__ __forceinline__ void store_p4(bf16* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
