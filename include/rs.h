@@ -14,6 +14,8 @@
  *    allocates or frees device memory; scratch space is the caller's `workspace`.
  *  - Every tensor is dense row-major.  Activations are [B][L][C] (sample, token,
  *    channel).  A Linear layer's weight is [out][in] and computes z W^T + b.
+ *  - Enumerated arguments (rs_dtype, rs_shift_op, rs_dist, rs_pool) are passed as int
+ *    and validated; an unknown value is RS_ERR_INVALID_ARG.
  *  - Element type: RS_F32 (float) or RS_BF16 (bfloat16 storage; all accumulation,
  *    softmax, LayerNorm statistics and scores are fp32).  Scores are always fp32,
  *    indices int32.
@@ -85,10 +87,10 @@ typedef struct {
   int heads;
   int hidden;
   float ln_eps;
-  rs_dtype dtype;
+  int dtype;              /* an rs_dtype */
   int has_cls;
-  rs_shift_op score_op;
-  rs_dist score_dist;
+  int score_op;           /* an rs_shift_op */
+  int score_dist;         /* an rs_dist */
   int attn_map;
 } rs_model_desc;
 
@@ -124,11 +126,11 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
 
 /* Representation shift with the L2 distance (Eq. (4)) of given tensors:
  * scores[r] = || fx[r,:] - x[r,:] ||_2 for every row r of [B*L][C]. */
-rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
+rs_status rs_score(const void* fx, const void* x, int B, int L, int C, int dtype,
                    float* scores, hipStream_t stream);
 /* Same with the distance of Sec. 3.3 chosen: scores[r] = D(fx[r,:], x[r,:]). */
-rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
-                        rs_dist dist, float* scores, hipStream_t stream);
+rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, int dtype,
+                        int dist, float* scores, hipStream_t stream);
 
 /* Multi-head attention alone (Sec. 3.1, Eq. (1), heads of 64 consecutive columns, scale
  * 1/8): qkv [B][L][3C] (Q | K | V, as the block's QKV projection writes them) ->
@@ -149,7 +151,7 @@ size_t rs_attention_workspace_bytes(const rs_model_desc* desc, int B, int L);
  * indices ascending to kept_idx [B][keep_k] and, if x_kept is not null, the rows
  * x[b, kept_idx[b, j], :] to x_kept [B][keep_k][C].  x may be null when x_kept is. */
 rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C,
-                         rs_dtype dtype, int keep_k, int has_cls,
+                         int dtype, int keep_k, int has_cls,
                          int32_t* kept_idx, void* x_kept, hipStream_t stream);
 
 /* Whole encoder with progressive pruning (Sec. 4.1 and 4.2 settings): blocks 0..depth-1
@@ -224,7 +226,7 @@ typedef struct {
   const void* w_head;
   const void* b_head;
   int n_out;
-  rs_pool pool;
+  int pool;               /* an rs_pool */
 } rs_head_weights;
 
 /* Patch embedding: images [B][frames][in_chans][height][width] (desc->dtype) ->

@@ -28,7 +28,7 @@ rs_status fail(rs_status s, const std::string& msg) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-size_t esize(rs_dtype dt) { return dt == RS_BF16 ? 2 : 4; }
+size_t esize(int dt) { return dt == RS_BF16 ? 2 : 4; }
 bool map_score(const rs_model_desc& d) {
   return d.score_op == RS_MAP_CLS || d.score_op == RS_MAP_MEAN;
 }
@@ -809,13 +809,13 @@ rs_status rs_block_forward(const rs_model_desc* desc, const rs_block_weights* w,
                     (size_t)desc->C * esize(desc->dtype), stream);
 }
 
-rs_status rs_score(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype, float* scores,
+rs_status rs_score(const void* fx, const void* x, int B, int L, int C, int dtype, float* scores,
                    hipStream_t stream) {
   return rs_score_dist(fx, x, B, L, C, dtype, RS_DIST_L2, scores, stream);
 }
 
-rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, rs_dtype dtype,
-                        rs_dist dist, float* scores, hipStream_t stream) {
+rs_status rs_score_dist(const void* fx, const void* x, int B, int L, int C, int dtype,
+                        int dist, float* scores, hipStream_t stream) {
   rs_status s;
   if (dtype != RS_F32 && dtype != RS_BF16) return fail(RS_ERR_INVALID_ARG, "unknown dtype");
   if (dist != RS_DIST_L2 && dist != RS_DIST_L1 && dist != RS_DIST_COS)
@@ -887,7 +887,7 @@ rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L,
   return RS_OK;
 }
 
-rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C, rs_dtype dtype,
+rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C, int dtype,
                          int keep_k, int has_cls, int32_t* kept_idx, void* x_kept,
                          hipStream_t stream) {
   rs_status s;
