@@ -165,8 +165,8 @@ rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C
  *  out_idx  [B][L_final] original token index of every output row.
  *  workspace/ws_bytes   >= rs_workspace_bytes(desc, depth, B, L).
  * Concurrency: the batch runs as n lanes, n the largest count up to the process-wide
- * maximum (rs_set_max_lanes) for which every lane keeps >= 1024 rows after the last
- * pruning (floor(B/n) * L_final >= 1024) -- lane i takes a contiguous share of the
+ * maximum (rs_set_max_lanes) for which every lane keeps >= 512 rows after the last
+ * pruning (floor(B/n) * L_final >= 512) -- lane i takes a contiguous share of the
  * samples, floor(B/n) or one more (the first B mod n lanes); lane 0 runs on `stream`, the
  * others on streams the library owns (default priority), forked from and joined back
  * into `stream` with events -- so one lane's memory-bound phases overlap another's

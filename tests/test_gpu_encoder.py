@@ -6,7 +6,7 @@ the same shapes (same kernels, deterministic), whose per-block results are check
 against the oracle on sampled samples with teacher forcing: the oracle block is fed the
 GPU's own block input, so each comparison measures one block's rounding.  The encoder
 runs a batch as n lanes (contiguous shares of the samples on n streams; n up to the
-process-wide maximum, default 2) when every lane keeps >= 1024 rows after the last
+process-wide maximum, default 2) when every lane keeps >= 512 rows after the last
 pruning; the reference chains run per lane, since a GEMM's split over K depends on its
 row count and so on the lane's batch."""
 import numpy as np
@@ -25,7 +25,7 @@ SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2],
 
 def lanes(B, L_final, max_lanes=2):
     n = max_lanes
-    while n > 1 and (B < n or (B // n) * L_final < 1024):
+    while n > 1 and (B < n or (B // n) * L_final < 512):
         n -= 1
     out, b0 = [], 0
     for i in range(n):

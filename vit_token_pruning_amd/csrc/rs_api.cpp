@@ -257,10 +257,11 @@ size_t carve_lane(const rs_model_desc& d, int B, int L, char* base, LaneWs* ws) 
 // kLaneMinRows rows after the last pruning, so one lane's memory-bound epilogues and
 // partial last rounds of workgroups overlap another lane's matrix work.  Smaller lanes
 // lose more to per-launch latency and extra K splits than the overlap gains (measured:
-// UMT-L at 2 x 98 final rows per lane 6.6 % slower, DeiT-S at 128 x 68 5.9 % faster).
+// UMT-L at 2 x 98 final rows per lane 6.6 % slower, DeiT-S at 128 x 68 5.9 % faster,
+// UMT-B at 4 x 196 2.2 % faster).
 // rs_block_forward uses one lane.
 constexpr int kMaxLanes = 4;
-constexpr long kLaneMinRows = 1024;
+constexpr long kLaneMinRows = 512;
 #ifndef RS_DEFAULT_LANES
 #define RS_DEFAULT_LANES 2
 #endif
