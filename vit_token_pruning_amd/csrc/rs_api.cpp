@@ -329,8 +329,8 @@ rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const
     int nj = 0;
     double bytes = 0.0;
     for (int i = b; i < b0 + n && i < b + rs::kMaxFoldJobs / 2; ++i) {
-      const rs_block_weights& w = blocks[i - b0];
-      const FoldWs fw = fold_of(d, ws, i - b0);
+      const rs_block_weights& w = blocks[i];
+      const FoldWs fw = fold_of(d, ws, i);
       jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, fw.wq, fw.cq, fw.dq, 3 * d.C};
       jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
       bytes += (2.0 * 3.0 * d.C + d.hidden) * d.C * esize(d.dtype);

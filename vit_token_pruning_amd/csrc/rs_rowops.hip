@@ -64,36 +64,54 @@ struct FoldArgs {
   int C;
 };
 
-// One wave per output row n of one job: W'[n][k] = W[n][k] * gamma[k] (rounded to the
-// storage type; only if the job has an output), c[n] = sum_k W'[n][k] (or the unrounded
-// sum_k W[n][k] gamma[k]), d[n] = sum_k W[n][k] beta[k] + b[n].
+// 16 lanes per output row n of one job (four rows per wave): W'[n][k] = W[n][k] * gamma[k]
+// (rounded to the storage type; only if the job has an output), c[n] = sum_k W'[n][k] (or
+// the unrounded sum_k W[n][k] gamma[k]), d[n] = sum_k W[n][k] beta[k] + b[n].  Lane s of
+// a row takes 8-element chunks s, s + 16, ... (at most 8 for C <= 1024) and requests all
+// of them before using any, so a wave keeps up to 32 row chunks in flight.
+constexpr int kFoldLanes = 16, kFoldRowsPerBlock = 256 / kFoldLanes;
 template <typename T>
 __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= fa.rows_before[fa.njobs]) return;  // whole wave
+  constexpr int kMaxCh = 1024 / 8 / kFoldLanes;
+  const int total = fa.rows_before[fa.njobs];
+  const int r = blockIdx.x * kFoldRowsPerBlock + (threadIdx.x / kFoldLanes);
+  const int sub = threadIdx.x % kFoldLanes;
+  // a row past the end repeats the last row's reads (its 16 lanes still take part in the
+  // row sums) and stores nothing
+  const bool live = r < total;
+  const int rr = live ? r : total - 1;
   int j = 0;
-  while (j + 1 < fa.njobs && r >= fa.rows_before[j + 1]) ++j;
+  while (j + 1 < fa.njobs && rr >= fa.rows_before[j + 1]) ++j;
   const FoldJob& jb = fa.job[j];
-  const int n = r - fa.rows_before[j], C = fa.C, nch = C >> 3;
+  const int n = rr - fa.rows_before[j], C = fa.C, nch = C >> 3;
   const T* w = static_cast<const T*>(jb.w) + (size_t)n * C;
-  T* wo = jb.w_out ? static_cast<T*>(jb.w_out) + (size_t)n * C : nullptr;
+  T* wo = jb.w_out && live ? static_cast<T*>(jb.w_out) + (size_t)n * C : nullptr;
+  Frag8<T> raw[kMaxCh];
+#pragma unroll
+  for (int i = 0; i < kMaxCh; ++i) {
+    const int ch = sub + i * kFoldLanes;
+    if (ch < nch) load_frag(raw[i], w + ch * 8);
+  }
   float c = 0.f, d = 0.f;
-  for (int ch = lane; ch < nch; ch += 64) {
+#pragma unroll
+  for (int i = 0; i < kMaxCh; ++i) {
+    const int ch = sub + i * kFoldLanes;
+    if (ch >= nch) break;
     float wv[8], g[8], b[8], o[8];
-    load8f(w + ch * 8, wv);
+    frag_to_f32(raw[i], wv);
     load8f(static_cast<const T*>(jb.gamma) + ch * 8, g);
     load8f(static_cast<const T*>(jb.beta) + ch * 8, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      o[e] = wo ? round_t<T>(wv[e] * g[e]) : wv[e] * g[e];
+      o[e] = jb.w_out ? round_t<T>(wv[e] * g[e]) : wv[e] * g[e];
       c += o[e];
       d = fmaf(wv[e], b[e], d);
     }
     if (wo) store8f(wo + ch * 8, o);
   }
-  c = wave_sum(c);
-  d = wave_sum(d);
-  if (lane == 0) {
+  c = sum16(c);
+  d = sum16(d);
+  if (sub == 0 && live) {
     jb.c[n] = c;
     jb.d[n] = d + to_f32(static_cast<const T*>(jb.bias)[n]);
   }
@@ -625,7 +643,7 @@ hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStrea
     fa.job[j] = jobs[j];
     fa.rows_before[j + 1] = fa.rows_before[j] + jobs[j].rows;
   }
-  const int grid = (fa.rows_before[njobs] + 3) / 4;
+  const int grid = (fa.rows_before[njobs] + kFoldRowsPerBlock - 1) / kFoldRowsPerBlock;
   if (dt == kBF16)
     fold_kernel<bf16><<<grid, 256, 0, stream>>>(fa);
   else
