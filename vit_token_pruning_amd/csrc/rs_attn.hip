@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   __shared__ __attribute__((aligned(1024))) char v0[64 * ROWBV], v1[64 * ROWBV];
 
   const int C = H * 64, ldqkv = 3 * C;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keep it (and the LDS addresses derived from it) scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   // launch index -> (query block, head, sample), query blocks fastest; each XCD gets a
   // contiguous range so the query blocks of one head re-read its K/V from one L2
@@ -103,12 +104,17 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
       store_frag(Vs + r * ROWBV + lc * CB, rv[i]);
     }
   };
+  // this lane's K row of tile kt is kt * 64 rows past its row of tile 0, except that the
+  // last tile of a ragged L clamps rows past the end
+  const T* krow0[2] = {kbase + (size_t)lr * ldqkv, kbase + (size_t)(lr + 32) * ldqkv};
   auto dload = [&](int kt, char* Ks, char* Vs) {
+    const size_t tstep = (size_t)kt * 64 * ldqkv;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = min(kt * 64 + lr + 32 * i, L - 1);
-      load_lds16(kbase + (size_t)key * ldqkv, Ks + (wave * 8 + 32 * i) * 128);
-      load_lds16(vbase + (size_t)key * ldqkv, Vs + (wave * 8 + 32 * i) * 128);
+      const T* kp = krow0[i] + tstep;
+      if (kt * 64 + 64 > L) kp = kbase + (size_t)min(kt * 64 + lr + 32 * i, L - 1) * ldqkv;
+      load_lds16(kp, Ks + (wave * 8 + 32 * i) * 128);
+      load_lds16(kp + C, Vs + (wave * 8 + 32 * i) * 128);
     }
   };
   auto kaddr = [&](const char* Ks, int r, int c) {
