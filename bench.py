@@ -102,9 +102,11 @@ def copy_probe(rs, torch):
 
 
 def summarize(dirs, workload):
-    """Per-kernel averages of the counters in rocprofv3 result databases; HBM traffic of each
-    kernel class from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by what the same
-    counters read for the 2 GiB copy probe (the gather dispatch with the largest grid)."""
+    """Per-kernel averages of the counters (and dispatch durations) in rocprofv3 result
+    databases; HBM traffic of each kernel class from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), scaled by what the same counters read for the 2 GiB copy probe (the gather
+    dispatch with the largest grid); matrix-core busy fraction from SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over all SIMDs) against 1024 SIMDs x the dispatch duration at 2.4 GHz."""
     import collections
     import glob
     import sqlite3
@@ -116,11 +118,18 @@ def summarize(dirs, workload):
             names = dict(cur.execute("select id, kernel_name from kernel_symbols"))
             disp = {r[0]: (r[1], r[2] * r[3] * r[4]) for r in cur.execute(
                 "select dispatch_id, kernel_id, grid_x, grid_y, grid_z from kernels")}
+            durs = collections.defaultdict(list)
+            for kid, dur in cur.execute("select kernel_id, duration from kernels"):
+                kc = kernel_class(names.get(kid, ""))
+                if kc is not None:
+                    durs[kc].append(dur)
             maxgrid = max((g for (kid, g) in disp.values() if kernel_class(names.get(kid, "")) == "gather"),
                           default=None)
+            has_sq = False
             for did, cname, cval in cur.execute(
                     "select dispatch_id, counter_name, sum(counter_value) from pmc_events "
                     "group by dispatch_id, counter_name"):
+                has_sq = has_sq or cname.startswith("SQ_")
                 kid, grid = disp.get(did, (None, 0))
                 kc = kernel_class(names.get(kid, ""))
                 if kc is None:
@@ -129,6 +138,9 @@ def summarize(dirs, workload):
                     probe[cname].append(cval)
                 else:
                     vals[kc][cname].append(cval)
+            if has_sq:   # durations of the run whose counters give the busy fractions
+                for kc, v in durs.items():
+                    vals[kc]["duration_ns"].extend(v)
     known = 8 * 16384 * 8192 * 2
     out = {"workload": workload, "kernels": {}}
     fac = {}
@@ -147,6 +159,8 @@ def summarize(dirs, workload):
                 t += row[c + "_bytes"]
         if "FETCH_SIZE_bytes" in row and "WRITE_SIZE_bytes" in row:
             row["traffic_bytes_per_launch"] = t
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in row and row.get("duration_ns"):
+            row["mfma_busy_frac"] = row["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * row["duration_ns"] * 2.4)
         out["kernels"][kc] = row
     out["kernel_sources_sha256"] = kernel_sources_sha256()
     return out
