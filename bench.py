@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roofline"
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
-                "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm", "gather": "hbm",
+                "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm",
                 "score": "hbm", "patch_embed": "mfma", "head": "mfma"}
 
 
@@ -81,17 +81,19 @@ def kernel_class(mangled: str):
         return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score", "4": "patch_embed",
                 "5": "head"}[m.group(2)]
     for key, name in (("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
-                      ("topk_kernel", "topk"), ("gather_kernel", "gather"), ("score_kernel", "score"),
-                      ("cls_rows_kernel", "patch_embed"), ("pool_kernel", "head")):
+                      ("topk_kernel", "topk"), ("score_kernel", "score"),
+                      ("cls_rows_kernel", "patch_embed"), ("pool_partial_kernel", "head"),
+                      ("pool_finish_kernel", "head")):
         if key in mangled:
             return name
     return None
 
 
 def copy_probe(rs, torch):
-    """A plain copy of known size through the library's gather kernel: 2 GiB of bf16 rows,
-    all kept (k = L), so the gather reads and writes exactly 2 GiB (+ 512 KiB of indices).
-    At 8x the 256 MB Infinity Cache, at most ~1/8 of the source can be cache-resident."""
+    """A plain copy of known size through rs_topk_gather (selection and copy in one launch):
+    2 GiB of bf16 rows, all kept (k = L), so the launch reads and writes exactly 2 GiB (+ the
+    512 KiB of scores and of indices).  At 8x the 256 MB Infinity Cache, at most ~1/8 of the
+    source can be cache-resident."""
     B, L, C = 8, 16384, 8192
     x = torch.randn(B, L, C, device="cuda").to(torch.bfloat16)
     s = torch.ones(B, L, device="cuda", dtype=torch.float32)
@@ -104,8 +106,9 @@ def copy_probe(rs, torch):
 def summarize(dirs, workload):
     """Per-kernel averages of the counters (and dispatch durations) in rocprofv3 result
     databases; HBM traffic of each kernel class from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), scaled by what the same counters read for the 2 GiB copy probe (the gather
-    dispatch with the largest grid); matrix-core busy fraction from SQ_VALU_MFMA_BUSY_CYCLES
+    dispatch), scaled by what the same counters read for the 2 GiB copy probe (a top-k
+    dispatch of over 100 us: the encoder's take tens); matrix-core busy fraction from
+    SQ_VALU_MFMA_BUSY_CYCLES
     (summed over all SIMDs) against 1024 SIMDs x the dispatch duration at 2.4 GHz."""
     import collections
     import glob
@@ -116,31 +119,29 @@ def summarize(dirs, workload):
         for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
             cur = sqlite3.connect(path).cursor()
             names = dict(cur.execute("select id, kernel_name from kernel_symbols"))
-            disp = {r[0]: (r[1], r[2] * r[3] * r[4]) for r in cur.execute(
-                "select dispatch_id, kernel_id, grid_x, grid_y, grid_z from kernels")}
+            disp = {r[0]: (r[1], r[2]) for r in cur.execute(
+                "select dispatch_id, kernel_id, duration from kernels")}
             durs = collections.defaultdict(list)
-            for kid, dur in cur.execute("select kernel_id, duration from kernels"):
+            for kid, dur in disp.values():
                 kc = kernel_class(names.get(kid, ""))
                 if kc is not None:
                     durs[kc].append(dur)
-            maxgrid = max((g for (kid, g) in disp.values() if kernel_class(names.get(kid, "")) == "gather"),
-                          default=None)
             has_sq = False
             for did, cname, cval in cur.execute(
                     "select dispatch_id, counter_name, sum(counter_value) from pmc_events "
                     "group by dispatch_id, counter_name"):
                 has_sq = has_sq or cname.startswith("SQ_")
-                kid, grid = disp.get(did, (None, 0))
+                kid, dur = disp.get(did, (None, 0))
                 kc = kernel_class(names.get(kid, ""))
                 if kc is None:
                     continue
-                if kc == "gather" and grid == maxgrid:
+                if kc == "topk" and dur > 100e3:
                     probe[cname].append(cval)
                 else:
                     vals[kc][cname].append(cval)
             if has_sq:   # durations of the run whose counters give the busy fractions
                 for kc, v in durs.items():
-                    vals[kc]["duration_ns"].extend(v)
+                    vals[kc]["duration_ns"].extend(d for d in v if not (kc == "topk" and d > 100e3))
     known = 8 * 16384 * 8192 * 2
     out = {"workload": workload, "kernels": {}}
     fac = {}
@@ -344,7 +345,7 @@ def main():
                     help="skip the single-lane per-kernel breakdown and context pass, so every "
                          "launch in the process is a timed-mode launch (for profiler runs)")
     ap.add_argument("--kernel", default="fc1", choices=[k for k in ("ln_prep", "qkv", "attention",
-                    "proj", "fc1", "fc2_score", "topk", "gather")],
+                    "proj", "fc1", "fc2_score", "topk")],
                     help="roofline kernel when --no-breakdown is given")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the Base / Attn / Ours comparison (context)")
@@ -405,7 +406,7 @@ def main():
     else:
         rs.set_max_lanes(1)
         for kname in rs.KERNELS:
-            if kname in ("score", "patch_embed", "head"):   # not launched by the encoder
+            if kname in ("score", "gather", "patch_embed", "head"):   # not launched by the encoder
                 continue
             with rs.KernelTimer(kname) as kt:
                 enc.forward(x)

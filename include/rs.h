@@ -301,7 +301,7 @@ typedef enum {
   RS_KERNEL_FC1 = 4,
   RS_KERNEL_FC2_SCORE = 5,
   RS_KERNEL_TOPK = 6,
-  RS_KERNEL_GATHER = 7,
+  RS_KERNEL_GATHER = 7,       /* reserved: kept rows are copied inside the top-k launch */
   RS_KERNEL_SCORE = 8,
   RS_KERNEL_PATCH = 9,        /* patch-embedding GEMM and class-token rows */
   RS_KERNEL_HEAD = 10,        /* final LayerNorm + pooling, and the head GEMM */

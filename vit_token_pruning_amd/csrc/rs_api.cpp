@@ -433,8 +433,8 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
 }
 
 // Top-k of each sample and compaction of the kept rows of x (-> x_kept, nullable) and of
-// an optional second row set (x2 -> x2_kept, e.g. the rows' LayerNorm statistics).  Large
-// batches do it in one launch; small ones copy with a separate all-rows grid.
+// an optional second row set (x2 -> x2_kept, e.g. the rows' LayerNorm statistics), in one
+// launch.
 rs_status run_select(int B, int L, int k, int has_cls, const float* scores, const float* part,
                      int P, int dist, float* scores_out, int32_t* kept, const int32_t* ids_in,
                      int32_t* ids_out, const void* x, void* x_kept, size_t row_bytes,
@@ -454,18 +454,10 @@ rs_status run_select(int B, int L, int k, int has_cls, const float* scores, cons
     cp[nc++] = {x2, x2_kept, (int)row_bytes2};
     copy_bytes += 2.0 * B * k * (double)row_bytes2;
   }
-  const bool fused = B >= rs::kTopkCopyMinBatch;
-  RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes + (fused ? copy_bytes : 0.0), st, [&] {
+  RS_HIP(timed(RS_KERNEL_TOPK, topk_bytes + copy_bytes, st, [&] {
     return rs::launch_topk(scores, part, P, dist, B, L, k, has_cls, scores_out, kept, ids_in,
-                           ids_out, cp, fused ? nc : 0, st);
+                           ids_out, cp, nc, st);
   }));
-  if (!fused) {
-    for (int i = 0; i < nc; ++i) {
-      RS_HIP(timed(RS_KERNEL_GATHER, 2.0 * B * k * (double)cp[i].row_bytes + B * k * 4.0, st, [&] {
-        return rs::launch_gather(cp[i].src, kept, cp[i].dst, B, L, k, cp[i].row_bytes, st);
-      }));
-    }
-  }
   return RS_OK;
 }
 

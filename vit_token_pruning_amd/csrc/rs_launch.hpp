@@ -162,13 +162,14 @@ inline int map_pad(int L) { return (L + 7) / 8 * 8; }
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
                              int dist, hipStream_t stream);
 
-// Per-sample exact top-k, one workgroup per sample.  Score source: `scores` [B][L], or
+// Per-sample exact top-k (one workgroup per sample, or topk_copy_split(B) when copying
+// rows).  Score source: `scores` [B][L], or
 // when `part` is not null the fp32 shift partials [B*L][dist_quantities(dist)][P] of the
 // GEMM epilogues, finished per distance (L2: sqrt of the sum; L1: the sum; cosine:
 // 1 - sum(a.b) / max(sqrt(sum a.a) sqrt(sum b.b), 1e-8)).  Writes the scores (if
-// scores_out), kept indices ascending [B][k], and (if ids_out) the composed original ids ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.
-// Then copies the kept rows of up to two row sets: dst[b][j] = src[b][kept[b][j]], rows
-// of row_bytes (a multiple of 16).
+// scores_out), kept indices ascending [B][k], and (if ids_out) the composed original ids
+// ids_out[b][j] = ids_in ? ids_in[b][kept] : kept.  Then copies the kept rows of up to two
+// row sets: dst[b][j] = src[b][kept[b][j]], rows of row_bytes (a multiple of 16).
 struct TopkCopy {
   const void* src;
   void* dst;
@@ -180,13 +181,15 @@ hipError_t launch_topk(const float* scores, const float* part, int P, int dist, 
                        int ncopies, hipStream_t stream);
 // partial quantities per slice of each distance (cosine: a.b, a.a, b.b)
 inline int dist_quantities(int dist) { return dist == 2 ? 3 : 1; }
-// Batches at least this large copy the kept rows inside the top-k launch (one workgroup
-// per sample); smaller ones use launch_gather, whose grid spans all rows.
-constexpr int kTopkCopyMinBatch = 32;
-
-// out[b][j][:] = x[b][kept[b][j]][:], rows of row_bytes (multiple of 16).
-hipError_t launch_gather(const void* x, const int32_t* kept, void* out, int B, int L, int k,
-                         int row_bytes, hipStream_t stream);
+// With row sets to copy, the top-k launch runs topk_copy_split(B) workgroups per sample:
+// each makes the same selection and copies its share of the kept rows, so that small
+// batches still spread the copy over about kTopkTargetWgs workgroups (the selection is a
+// few passes over one sample's L keys in LDS; the copy is what needs the bandwidth).
+constexpr int kTopkTargetWgs = 128, kTopkMaxSplit = 64;
+inline int topk_copy_split(int B) {
+  const int g = (kTopkTargetWgs + B - 1) / B;
+  return g < 1 ? 1 : (g > kTopkMaxSplit ? kTopkMaxSplit : g);
+}
 
 // ids[b][i] = i
 hipError_t launch_iota(int32_t* ids, int B, int L, hipStream_t stream);

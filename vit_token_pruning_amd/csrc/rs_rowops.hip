@@ -1,6 +1,6 @@
 // Row-wise and selection kernels: LayerNorm preparation (row statistics, folded weights),
-// the standalone representation-shift score, the per-sample exact top-k, and the
-// compaction of kept rows.
+// the standalone representation-shift score, and the per-sample exact top-k with the
+// compaction of the kept rows.
 //
 // Method: "Representation Shift: Unifying Token Compression with FlashAttention" (arXiv
 // HTML).  LayerNorm is the LN of Sec. 3.3, Eqs. (5) and (6); the score is Eq. (4) with
@@ -363,7 +363,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return before + incl - v;
 }
 
-// One workgroup per sample.  Selection of the k largest keys (ties to the lower index): the
+// One workgroup per sample, or G per sample when rows are copied (see below).  Selection
+// of the k largest keys (ties to the lower index): the
 // exact k-th largest key T by a 4-pass 8-bit radix select (MSB first) over an LDS
 // histogram; kept = every key above T plus the lowest-index keys equal to it.
 //  - L <= kWaveMaxL: wave 0 alone, 4 keys per lane, lane scans instead of workgroup
@@ -371,15 +372,19 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 //  - longer L: all threads, one histogram pass per 8 bits with workgroup barriers.
 // Kept indices are emitted in ascending index order (block scans), composed with ids_in,
 // and listed in LDS; then the workgroup copies up to two row sets of the kept rows
-// (RowCopy: 16-byte units per row), so selection and compaction are one launch.  Integer
-// work only: deterministic.
+// (RowCopy: 16-byte units per row), so selection and compaction are one launch.  With G
+// workgroups per sample every one of them makes the (deterministic, integer-only)
+// selection, copies its contiguous share of the kept rows, and only the first writes the
+// scores, indices and ids.
 struct RowCopy {
   const char* src;  // [L] rows of `units` 16-byte units per sample, or null
   char* dst;        // [k] rows per sample
   int units;
 };
 
-__device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list, int b, int L, int k) {
+// Copies kept rows j in [j0, j1) of sample b: dst row j = src row list[j].
+__device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list, int b, int L, int k,
+                                          int j0, int j1) {
   if (!c.src) return;
   const int upr = c.units;
   const u32x4* src = reinterpret_cast<const u32x4*>(c.src) + (long long)b * L * upr;
@@ -387,24 +392,24 @@ __device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list
   constexpr int U = 8;  // rows in flight per thread
   const int tid = threadIdx.x;
   if (upr <= kTopkThreads) {
-    // thread -> (row offset r, unit cu), fixed; rows r, r + rpi, r + 2 rpi, ...
+    // thread -> (row offset r, unit cu), fixed; rows j0 + r, j0 + r + rpi, ...
     const int rpi = kTopkThreads / upr, r = tid / upr, cu = tid - r * upr;
     if (r >= rpi) return;
-    for (int j0 = r; j0 < k; j0 += rpi * U) {
+    for (int jb = j0 + r; jb < j1; jb += rpi * U) {
       u32x4 v[U];
 #pragma unroll
       for (int q = 0; q < U; ++q) {
-        const int j = j0 + q * rpi;
-        if (j < k) v[q] = src[(long long)list[j] * upr + cu];
+        const int j = jb + q * rpi;
+        if (j < j1) v[q] = src[(long long)list[j] * upr + cu];
       }
 #pragma unroll
       for (int q = 0; q < U; ++q) {
-        const int j = j0 + q * rpi;
-        if (j < k) dst[(long long)j * upr + cu] = v[q];
+        const int j = jb + q * rpi;
+        if (j < j1) dst[(long long)j * upr + cu] = v[q];
       }
     }
   } else {
-    for (int j = 0; j < k; ++j) {
+    for (int j = j0; j < j1; ++j) {
       const u32x4* s = src + (long long)list[j] * upr;
       u32x4* d = dst + (long long)j * upr;
       for (int cu = tid; cu < upr; cu += kTopkThreads) d[cu] = s[cu];
@@ -415,12 +420,17 @@ __device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, const float* __restrict__ part, int P, int dist, int L,
     int k, int has_cls, float* __restrict__ scores_out, int32_t* __restrict__ kept,
-    const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out, RowCopy c0, RowCopy c1) {
+    const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out, RowCopy c0, RowCopy c1,
+    int G) {
   __shared__ __attribute__((aligned(16))) uint32_t keys[RS_MAX_TOKENS];  // keys, then the kept list
   __shared__ uint32_t hist[256];
   __shared__ int wsum[kTopkThreads / 64];
   __shared__ uint32_t sel[2];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  // G workgroups per sample: each makes the same selection; workgroup g copies kept rows
+  // [g k / G, (g + 1) k / G), and workgroup 0 alone writes scores, indices and ids
+  const int b = blockIdx.x / G, g = blockIdx.x - b * G, tid = threadIdx.x;
+  const bool lead = g == 0;
+  const int cj0 = (int)((long long)g * k / G), cj1 = (int)((long long)(g + 1) * k / G);
   const size_t rb = (size_t)b * L;
 
   for (int i = tid; i < L; i += kTopkThreads) {
@@ -439,7 +449,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     } else {
       s = scores[rb + i];
     }
-    if (scores_out) scores_out[rb + i] = s;
+    if (scores_out && lead) scores_out[rb + i] = s;
     keys[i] = (has_cls && i == 0) ? 0xFFFFFFFFu : order_key(s);
   }
   __syncthreads();
@@ -513,8 +523,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       for (int q = 0; q < 4; ++q) {
         if (((keep >> q) & 1u) && pos < (uint32_t)k) {
           const int i = 4 * lane + q;
-          kb[pos] = i;
-          if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+          if (lead) {
+            kb[pos] = i;
+            if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+          }
           keys[pos] = (uint32_t)i;  // kept list (the keys were read into registers above)
           ++pos;
         }
@@ -522,8 +534,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
     if (!c0.src && !c1.src) return;
     __syncthreads();
-    copy_rows(c0, keys, b, L, k);
-    copy_rows(c1, keys, b, L, k);
+    copy_rows(c0, keys, b, L, k, cj0, cj1);
+    copy_rows(c1, keys, b, L, k, cj0, cj1);
     return;
   }
   {
@@ -581,34 +593,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   int32_t* kb = kept + (size_t)b * k;
   for (int i = i0; i < i1; ++i) {
     if (((keepbits >> (i - i0)) & 1u) && pos < k) {
-      kb[pos] = i;
-      if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+      if (lead) {
+        kb[pos] = i;
+        if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
+      }
       keys[pos] = (uint32_t)i;  // kept list (every key read above is done: scan barrier)
       ++pos;
     }
   }
   if (!c0.src && !c1.src) return;
   __syncthreads();
-  copy_rows(c0, keys, b, L, k);
-  copy_rows(c1, keys, b, L, k);
-}
-
-// ---------------------------------------------------------------- gather
-// One 16-byte unit per thread, grid-stride; consecutive threads copy consecutive
-// units of one kept row.
-__global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
-                                                     const int32_t* __restrict__ kept,
-                                                     char* __restrict__ out, int L, int k,
-                                                     int units_per_row, long long total) {
-  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total;
-       u += (long long)gridDim.x * 256) {
-    const long long row = u / units_per_row;
-    const int c = (int)(u - row * units_per_row);
-    const long long b = row / k;
-    const long long src = b * L + kept[row];
-    reinterpret_cast<u32x4*>(out)[u] =
-        reinterpret_cast<const u32x4*>(x + src * (long long)units_per_row * 16)[c];
-  }
+  copy_rows(c0, keys, b, L, k, cj0, cj1);
+  copy_rows(c1, keys, b, L, k, cj0, cj1);
 }
 
 __global__ void iota_kernel(int32_t* ids, int L, long long total) {
@@ -705,16 +701,9 @@ hipError_t launch_topk(const float* scores, const float* part, int P, int dist, 
   for (int i = 0; i < ncopies && i < 2; ++i)
     c[i] = {static_cast<const char*>(copies[i].src), static_cast<char*>(copies[i].dst),
             copies[i].row_bytes / 16};
-  topk_kernel<<<B, kTopkThreads, 0, stream>>>(scores, part, P, dist, L, k, has_cls, scores_out,
-                                              kept, ids_in, ids_out, c[0], c[1]);
-  return hipGetLastError();
-}
-hipError_t launch_gather(const void* x, const int32_t* kept, void* out, int B, int L, int k,
-                         int row_bytes, hipStream_t stream) {
-  const int upr = row_bytes / 16;
-  const long long total = (long long)B * k * upr;
-  gather_kernel<<<grid_for(total), 256, 0, stream>>>(static_cast<const char*>(x), kept,
-                                                     static_cast<char*>(out), L, k, upr, total);
+  const int G = ncopies > 0 ? topk_copy_split(B) : 1;
+  topk_kernel<<<B * G, kTopkThreads, 0, stream>>>(scores, part, P, dist, L, k, has_cls, scores_out,
+                                                  kept, ids_in, ids_out, c[0], c[1], G);
   return hipGetLastError();
 }
 
