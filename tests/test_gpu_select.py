@@ -58,12 +58,15 @@ def test_topk_gather_edges(B, L, k, cls, kind):
     _run(B, L, k, cls, kind, seed=L + 3 * k + B)
 
 
-# Batches of >= 32 samples copy the kept rows inside the top-k launch; L <= 256 takes the
-# rank path, longer L the radix select.  Row widths of 3 to 1032 16-byte units.
+# The kept rows are copied inside the top-k launch by ceil(128 / B) (at most 64) workgroups
+# per sample, each copying a contiguous share; L <= 256 takes the single-wave selection,
+# longer L the 1024-thread radix select.  Row widths of 3 to 1032 16-byte units (over 1024
+# units a row is copied by all threads in turn); shares of zero rows when k < the split.
 FUSED = [(64, 1568, 784, False, 256), (40, 2000, 37, True, 64), (32, 1025, 1, True, 1024),
          (33, 300, 299, False, 8), (32, 1024, 1024, True, 384), (48, 16384, 9000, False, 8),
          (32, 256, 255, False, 8192), (36, 256, 1, True, 16), (32, 257, 128, True, 24),
-         (32, 40, 20, False, 8256)]
+         (32, 40, 20, False, 8256), (1, 1568, 700, False, 8256), (3, 300, 299, True, 8192),
+         (7, 97, 5, True, 384), (2, 2352, 1882, False, 768), (129, 197, 138, True, 384)]
 
 
 @pytest.mark.parametrize("B,L,k,cls,C", FUSED)
