@@ -184,3 +184,49 @@ def test_encoder_more_lanes(n):
         check_encoder(wl, [0, 63], max_lanes=n)
     finally:
         rs.set_max_lanes(2)
+
+
+def test_encoder_concurrent_calls_on_two_streams():
+    """Two host threads, each with its own stream and workspace, run the encoder at the same
+    time (two lanes each, so both calls also fork onto the library's lane stream); every
+    result equals the single-threaded run of the same input bit for bit."""
+    import dataclasses
+    import threading
+    import torch
+    import vit_token_pruning_amd as rs
+    wl = dataclasses.replace(synth.WORKLOADS["deit_s"], B=45, L=97, depth=3, prune_layers=(1,),
+                             keep_ratios=(0.7,))
+    spec = spec_of(wl)
+    wd = [weights_to_dev(w, wl.dtype) for w in synth.make_encoder_weights(wl, 0)]
+    xs = [to_dev(synth.make_input(wl, seed), wl.dtype) for seed in (0, 1)]
+    refs = []
+    for x in xs:
+        out, idx = rs.Encoder(spec, wd, wl.B, wl.L, wl.prune_layers, wl.keep_ratios).forward(x)
+        torch.cuda.synchronize()
+        refs.append((out.clone(), idx.clone()))
+    encs = [rs.Encoder(spec, wd, wl.B, wl.L, wl.prune_layers, wl.keep_ratios) for _ in xs]
+    streams = [torch.cuda.Stream() for _ in xs]
+    torch.cuda.synchronize()
+    results, errors = [[], []], []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(4):
+                    out, idx = encs[i].forward(xs[i])
+                    results[i].append((out.clone(), idx.clone()))
+            streams[i].synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(xs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for i, (ref_out, ref_idx) in enumerate(refs):
+        assert len(results[i]) == 4
+        for out, idx in results[i]:
+            assert torch.equal(out, ref_out) and torch.equal(idx, ref_idx), f"thread {i}"
