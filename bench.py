@@ -108,12 +108,14 @@ def summarize(dirs, workload):
     databases; HBM traffic of each kernel class from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), scaled by what the same counters read for the 2 GiB copy probe (a top-k
     dispatch of over 100 us: the encoder's take tens); matrix-core busy fraction from
-    SQ_VALU_MFMA_BUSY_CYCLES
-    (summed over all SIMDs) against 1024 SIMDs x the dispatch duration at 2.4 GHz."""
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over all SIMDs) against 1024 SIMDs x the dispatch
+    duration at 2.4 GHz, also per launch shape ("by_grid": dispatches grouped by their grid
+    size in work-items, which tells the prune stages apart)."""
     import collections
     import glob
     import sqlite3
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    by_grid = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(list)))
     probe = collections.defaultdict(list)
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
@@ -121,7 +123,10 @@ def summarize(dirs, workload):
             names = dict(cur.execute("select id, kernel_name from kernel_symbols"))
             disp = {r[0]: (r[1], r[2]) for r in cur.execute(
                 "select dispatch_id, kernel_id, duration from kernels")}
+            grids = {r[0]: r[1] * r[2] * r[3] for r in cur.execute(
+                "select dispatch_id, grid_x, grid_y, grid_z from kernels")}
             durs = collections.defaultdict(list)
+            per_disp = collections.defaultdict(dict)
             for kid, dur in disp.values():
                 kc = kernel_class(names.get(kid, ""))
                 if kc is not None:
@@ -139,9 +144,16 @@ def summarize(dirs, workload):
                     probe[cname].append(cval)
                 else:
                     vals[kc][cname].append(cval)
+                    per_disp[did][cname] = cval
             if has_sq:   # durations of the run whose counters give the busy fractions
                 for kc, v in durs.items():
                     vals[kc]["duration_ns"].extend(d for d in v if not (kc == "topk" and d > 100e3))
+                for did, cs in per_disp.items():
+                    kid, dur = disp[did]
+                    g = by_grid[kernel_class(names.get(kid, ""))][grids[did]]
+                    g["duration_ns"].append(dur)
+                    for cname, cval in cs.items():
+                        g[cname].append(cval)
     known = 8 * 16384 * 8192 * 2
     out = {"workload": workload, "kernels": {}}
     fac = {}
@@ -162,6 +174,14 @@ def summarize(dirs, workload):
             row["traffic_bytes_per_launch"] = t
         if "SQ_VALU_MFMA_BUSY_CYCLES" in row and row.get("duration_ns"):
             row["mfma_busy_frac"] = row["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * row["duration_ns"] * 2.4)
+        if kc in by_grid:
+            row["by_grid"] = {}
+            for grid, gs in sorted(by_grid[kc].items(), reverse=True):
+                g = {c: sum(v) / len(v) for c, v in gs.items()}
+                g["dispatches"] = len(gs["duration_ns"])
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in g and g["duration_ns"]:
+                    g["mfma_busy_frac"] = g["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * g["duration_ns"] * 2.4)
+                row["by_grid"][str(grid)] = g
         out["kernels"][kc] = row
     out["kernel_sources_sha256"] = kernel_sources_sha256()
     return out
