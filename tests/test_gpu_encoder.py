@@ -20,7 +20,8 @@ from rs_testutil import (check_block_output, check_scores, kept_admissible, spec
 pytestmark = pytest.mark.gpu
 
 SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2],
-           "deit_s512": [511], "umt_l12f_ret": [13]}
+           "deit_s512": [511], "umt_l12f_ret": [13], "deit_t512": [0, 300], "deit_b512": [400],
+           "umt_b12f_qa": [19]}
 
 
 def lanes(B, L_final, max_lanes=2):
@@ -94,7 +95,8 @@ def check_encoder(wl, samples, max_lanes=2):
     print(f"{wl.name} B{wl.B}: exact kept-set agreement {exact}/{total} sampled prune stages")
 
 
-@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l", "deit_s512", "umt_l12f_ret"])
+@pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l", "deit_s512", "umt_l12f_ret",
+                                  "deit_t512", "deit_b512", "umt_b12f_qa"])
 def test_encoder_full_size(name):
     check_encoder(synth.WORKLOADS[name], SAMPLED[name])
 
