@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 SAMPLED = {"deit_s": [0, 255], "deit_b": [0, 127], "umt_b": [5], "umt_l": [2],
            "deit_s512": [511], "umt_l12f_ret": [13], "deit_t512": [0, 300], "deit_b512": [400],
-           "umt_b12f_qa": [19]}
+           "umt_b12f_qa": [19], "umt_b12f_ret": [3], "umt_l12f_qa": [7]}
 
 
 def lanes(B, L_final, max_lanes=2):
@@ -96,7 +96,8 @@ def check_encoder(wl, samples, max_lanes=2):
 
 
 @pytest.mark.parametrize("name", ["deit_s", "deit_b", "umt_b", "umt_l", "deit_s512", "umt_l12f_ret",
-                                  "deit_t512", "deit_b512", "umt_b12f_qa"])
+                                  "deit_t512", "deit_b512", "umt_b12f_qa", "umt_b12f_ret",
+                                  "umt_l12f_qa"])
 def test_encoder_full_size(name):
     check_encoder(synth.WORKLOADS[name], SAMPLED[name])
 
