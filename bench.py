@@ -472,10 +472,12 @@ def main():
                                "avg_launch_us": round(kt1.total_ms * 1e3 / max(1, kt1.launches), 3)}
 
     # algorithmic flop of one step under the schedule: 2 * (12 L C^2 + 2 L^2 C) per sample-block
-    from_sched = 0.0
+    # and the token-blocks one sample passes through (tokens entering each block)
+    from_sched, token_blocks = 0.0, 0
     L = wl.L
     for b in range(wl.depth):
         from_sched += 2.0 * (12 * L * wl.C ** 2 + 2 * L * L * wl.C)
+        token_blocks += L
         if b in wl.prune_layers:
             L = int(np.floor(wl.keep_ratios[list(wl.prune_layers).index(b)] * L + 0.5))
     tflops = from_sched * wl.B / (ms_step / 1e3) / 1e12
@@ -490,6 +492,7 @@ def main():
                    "depth": wl.depth, "prune_after_blocks": list(wl.prune_layers),
                    "keep_ratios": list(wl.keep_ratios), "has_cls": wl.has_cls},
         "tokens_per_s": round(value * wl.L, 1),
+        "token_blocks_per_s": round(value * token_blocks, 1),
         "encoder_tflops": round(tflops, 2),
         "roofline": roof,
         "kernel_ms_per_step": {k: round(v["ms"], 4) for k, v in per.items()},  # single lane
