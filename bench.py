@@ -26,7 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roofline"
-PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
+PEAK = {"mfma": 2500.0, "hbm": 8000.0}
+BREAKDOWN_STEPS = 5   # steps per kernel class in the single-lane breakdown (fc1 and fc2 are close)   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
                 "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm",
                 "score": "hbm", "patch_embed": "mfma", "head": "mfma"}
@@ -364,7 +365,7 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the single-lane per-kernel breakdown and context pass, so every "
                          "launch in the process is a timed-mode launch (for profiler runs)")
-    ap.add_argument("--kernel", default="fc1", choices=[k for k in ("ln_prep", "qkv", "attention",
+    ap.add_argument("--kernel", default="fc2_score", choices=[k for k in ("ln_prep", "qkv", "attention",
                     "proj", "fc1", "fc2_score", "topk")],
                     help="roofline kernel when --no-breakdown is given")
     ap.add_argument("--no-compare", action="store_true",
@@ -418,8 +419,8 @@ def main():
     def rate(work, ms):
         return work / (ms / 1e3) / (1e12 if bound == "mfma" else 1e9)
 
-    # per-kernel breakdown (one step per kernel class, single lane so launches do not
-    # overlap) to find the dominant kernel
+    # per-kernel breakdown (BREAKDOWN_STEPS steps per kernel class, averaged; single lane so
+    # launches do not overlap) to find the dominant kernel
     per, kt1 = {}, None
     if args.no_breakdown:
         dominant = args.kernel
@@ -429,8 +430,10 @@ def main():
             if kname in ("score", "gather", "patch_embed", "head"):   # not launched by the encoder
                 continue
             with rs.KernelTimer(kname) as kt:
-                enc.forward(x)
-            per[kname] = {"ms": kt.total_ms, "launches": kt.launches, "work": kt.work}
+                for _ in range(BREAKDOWN_STEPS):
+                    enc.forward(x)
+            per[kname] = {"ms": kt.total_ms / BREAKDOWN_STEPS, "launches": kt.launches // BREAKDOWN_STEPS,
+                          "work": kt.work / BREAKDOWN_STEPS}
         dominant = max(per, key=lambda k: per[k]["ms"])
         log("per-kernel ms/step (single lane):", {k: round(v["ms"], 4) for k, v in per.items()},
             "dominant:", dominant)
