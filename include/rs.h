@@ -28,6 +28,8 @@
  *    Nothing is printed, nothing aborts, no C++ exception crosses the ABI.
  *    rs_last_error() returns a message for the calling thread's last failure.
  *  - Calls are re-entrant; concurrent calls need distinct workspaces and outputs.
+ *  - No call works in place: outputs and the workspace must not overlap the inputs or
+ *    each other (overlapping buffers give undefined results; this is not checked).
  *  - Limits (else RS_ERR_UNSUPPORTED): head dim 64 (C == heads*64), C % 64 == 0,
  *    C <= RS_MAX_WIDTH, hidden % 64 == 0, 1 <= L <= RS_MAX_TOKENS, and
  *    B*L*max(3C, hidden) < 2^31.
