@@ -7,10 +7,14 @@ LayerNorms, QKV GEMM, fused attention, projection, fc1+GELU, fc2 with the fused 
 and the three top-k + compaction stages.  Inputs and weights are synthetic (seeded,
 N(0,1) inputs, N(0, 0.02^2) weights) and resident in HBM before timing starts.
 
-Prints one JSON line.  Also measured inside the timed region: the dominant kernel's
-summed HIP-event time (events recorded on the stream the kernel is launched on) and its
-algorithmic work, giving the roofline fraction; and the fp64 CPU oracle on a bounded
-sample of the same workload (cpu_baseline).
+Prints one JSON line.  `value` comes from K timed steps with nothing else instrumented.
+The roofline figure comes from the same K steps run again with the dominant kernel's
+launches bracketed by HIP events on the stream each launch runs on (its summed time and
+algorithmic work; `instrumented_ms_per_step` shows what the events cost).  Context keys:
+the single-lane per-kernel breakdown, the standalone HBM-bound kernels (`hbm_kernels`), the
+other workloads (`configs`: the fp32 DeiT-T block, DeiT-B, UMT-B, UMT-L), the pages' Base /
+Attn / Ours structure, the whole forward pass, and the fp64 CPU oracle on the same workload
+(`cpu_baseline`).
 
     python bench.py [--steps K] [--warmup W] [--workload deit_s] [--no-cpu-baseline]
 """
@@ -26,8 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roofline"
-PEAK = {"mfma": 2500.0, "hbm": 8000.0}
-BREAKDOWN_STEPS = 5   # steps per kernel class in the single-lane breakdown (fc1 and fc2 are close)   # bf16 dense TFLOP/s, HBM GB/s (MI355X published)
+# MI355X published peaks: dense bf16 and fp32 matrix-core TFLOP/s, HBM GB/s
+PEAK = {"mfma": 2500.0, "mfma_f32": 157.3, "hbm": 8000.0}
+BREAKDOWN_STEPS = 5   # steps per kernel class in the single-lane breakdown (fc1 and fc2 are close)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
                 "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm",
                 "score": "hbm", "patch_embed": "mfma", "head": "mfma"}
@@ -37,9 +42,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, x, blocks, budget_s=12.0):
-    """The fp64 oracle encoder on as many whole samples as fit a ~10-30 s budget."""
-    import numpy as np
+def cpu_baseline(wl, x, blocks, budget_s=30.0):
+    """The fp64 oracle encoder on whole samples of the same workload, the full batch when
+    it fits a ~30 s budget, else as many samples as fit."""
     from oracle import rs_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -56,6 +61,7 @@ def cpu_baseline(wl, x, blocks, budget_s=12.0):
         if t_total >= budget_s:
             break
     return {"value": n / t_total, "unit": f"{wl.unit}/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{n} of {wl.B} {wl.unit}s of the same workload through the full "
                       f"{wl.depth}-block pruned encoder, fp64 NumPy, {t_total:.1f} s"}
 
@@ -352,6 +358,122 @@ def whole_forward(wl, spec, blocks, steps, rs, torch):
             "note": "patch embedding + the pruned encoder + final LN + head; context only"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def schedule_work(wl):
+    """Algorithmic flop of one step under the schedule, 2 (12 L C^2 + 2 L^2 C) per
+    sample-block, and the token-blocks one sample passes through."""
+    import numpy as np
+    flop, token_blocks = 0.0, 0
+    L = wl.L
+    for b in range(wl.depth):
+        flop += 2.0 * (12 * L * wl.C ** 2 + 2 * L * L * wl.C)
+        token_blocks += L
+        if b in wl.prune_layers:
+            L = int(np.floor(wl.keep_ratios[list(wl.prune_layers).index(b)] * L + 0.5))
+    return flop * wl.B, token_blocks
+
+
+def breakdown(enc, x, rs, steps):
+    """Per-kernel ms/step with the batch on one lane (launches do not overlap); restores
+    the lane setting."""
+    prev = rs.get_max_lanes()
+    rs.set_max_lanes(1)
+    per = {}
+    try:
+        for kname in rs.KERNELS:
+            if kname in ("score", "gather", "patch_embed", "head"):   # not launched by the encoder
+                continue
+            with rs.KernelTimer(kname) as kt:
+                for _ in range(steps):
+                    enc.forward(x)
+            per[kname] = {"ms": kt.total_ms / steps, "launches": kt.launches // steps,
+                          "work": kt.work / steps}
+    finally:
+        rs.set_max_lanes(prev)
+    return per
+
+
+def time_steps(fn, n, torch):
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def other_config(name, steps, rs, torch):
+    """One more encoder workload (value, ms/step and the dominant kernel's rate with the
+    batch on one lane), for the bench line's `configs` key."""
+    import synth
+    wl = synth.WORKLOADS[name]
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(synth.make_input(wl, 0)).cuda().to(dt)
+    blocks = [{n: torch.from_numpy(v).cuda().to(dt) for n, v in w.items()}
+              for w in synth.make_encoder_weights(wl, 0)]
+    spec = rs.ModelSpec(wl.C, wl.heads, wl.hidden, dt, wl.has_cls, wl.ln_eps)
+    enc = rs.Encoder(spec, blocks, wl.B, wl.L, wl.prune_layers, wl.keep_ratios)
+    for _ in range(3):
+        enc.forward(x)
+    ms = time_steps(lambda: enc.forward(x), steps, torch)
+    per = breakdown(enc, x, rs, 2)
+    dom = max(per, key=lambda k: per[k]["ms"])
+    flop, token_blocks = schedule_work(wl)
+    ach = per[dom]["work"] / (per[dom]["ms"] / 1e3) / 1e12
+    out = {"value": round(wl.B / (ms / 1e3), 2), "unit": f"{wl.unit}/s", "ms_per_step": round(ms, 4),
+           "steps": steps, "dtype": wl.dtype, "batch": wl.B, "tokens": wl.L, "C": wl.C,
+           "depth": wl.depth, "tokens_per_s": round(wl.B * wl.L / (ms / 1e3), 1),
+           "encoder_tflops": round(flop / (ms / 1e3) / 1e12, 2),
+           "kernel_ms_per_step": {k: round(v["ms"], 4) for k, v in per.items()},
+           "dominant_single_lane": {"kernel": dom, "achieved": round(ach, 2), "unit": "TFLOP/s",
+                                    "frac": round(ach / PEAK["mfma"], 4)}}
+    log(f"config {name}: {out['value']} {out['unit']}, {ms:.4f} ms/step, dominant {dom} "
+        f"{out['dominant_single_lane']['frac']}")
+    del enc, blocks, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def block_config(steps, rs, torch):
+    """The single fp32 DeiT-T block (batch 2, 197 tokens, keep 138): rs_block_forward with
+    scoring, top-k and compaction per step; rate against the fp32 matrix-core peak."""
+    import numpy as np
+    import synth
+    wl = synth.WORKLOADS["deit_t_block"]
+    x = torch.from_numpy(synth.make_input(wl, 0)).cuda()
+    w = {n: torch.from_numpy(v).cuda() for n, v in synth.make_block_weights(wl, 0, 0).items()}
+    spec = rs.ModelSpec(wl.C, wl.heads, wl.hidden, torch.float32, wl.has_cls, wl.ln_eps)
+    k = int(np.floor(wl.keep_ratios[0] * wl.L + 0.5))
+    ws = torch.empty(rs.workspace_bytes(spec, 1, wl.B, wl.L), dtype=torch.uint8, device="cuda")
+    for _ in range(10):
+        rs.block_forward(spec, w, x, k, workspace=ws)
+    ms = time_steps(lambda: rs.block_forward(spec, w, x, k, workspace=ws), steps, torch)
+    flop = 2.0 * wl.B * (12 * wl.L * wl.C ** 2 + 2 * wl.L ** 2 * wl.C)
+    ach = flop / (ms / 1e3) / 1e12
+    return {"value": round(wl.B / (ms / 1e3), 2), "unit": "sample-blocks/s",
+            "blocks_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 5), "steps": steps,
+            "dtype": "f32", "batch": wl.B, "tokens": wl.L, "keep_k": k, "C": wl.C,
+            "tokens_per_s": round(wl.B * wl.L / (ms / 1e3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK["mfma_f32"],
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK["mfma_f32"], 5)},
+            "note": "one block + score + top-k + compaction per step (launch-latency bound at "
+                    "this size)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,8 +485,8 @@ def main():
                     help="time rs_score and rs_topk_gather alone at the prune-stage shapes "
                          "(HBM-bound kernels, rotating >= 512 MiB of inputs); prints one JSON line")
     ap.add_argument("--no-breakdown", action="store_true",
-                    help="skip the single-lane per-kernel breakdown and context pass, so every "
-                         "launch in the process is a timed-mode launch (for profiler runs)")
+                    help="skip the single-lane per-kernel breakdown and every context pass, so "
+                         "every launch in the process is a timed-mode launch (for profiler runs)")
     ap.add_argument("--kernel", default="fc2_score", choices=[k for k in ("ln_prep", "qkv", "attention",
                     "proj", "fc1", "fc2_score", "topk")],
                     help="roofline kernel when --no-breakdown is given")
@@ -372,8 +494,12 @@ def main():
                     help="skip the Base / Attn / Ours comparison (context)")
     ap.add_argument("--no-whole", action="store_true",
                     help="skip the whole-forward context (patch embedding + encoder + head)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (DeiT-T fp32 block, DeiT-B, UMT-B, UMT-L)")
+    ap.add_argument("--no-hbm", action="store_true",
+                    help="skip the standalone rs_score / rs_topk_gather measurement")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a 256 MiB copy through the gather kernel (counter calibration)")
+                    help="also run a 2 GiB copy through the gather kernel (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 --pmc result directories and exit (no GPU use)")
     args = ap.parse_args()
@@ -386,7 +512,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
@@ -394,7 +519,7 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     if wl.depth == 1:
-        sys.exit("pick an encoder workload")
+        sys.exit("pick an encoder workload (the single block is reported under `configs`)")
     if args.standalone:
         torch.cuda.set_device(0)
         res = standalone(wl, args.steps)
@@ -416,79 +541,64 @@ def main():
         enc.forward(x)
     torch.cuda.synchronize()
 
-    def rate(work, ms):
-        return work / (ms / 1e3) / (1e12 if bound == "mfma" else 1e9)
+    # timed region: K steps of the encoder as it runs by default (two lanes when the batch
+    # is large enough), nothing else instrumented
+    ms_step = time_steps(lambda: enc.forward(x), args.steps, torch)
+    value = wl.B / (ms_step / 1e3)
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step, {value:.1f} {wl.unit}/s")
 
-    # per-kernel breakdown (BREAKDOWN_STEPS steps per kernel class, averaged; single lane so
-    # launches do not overlap) to find the dominant kernel
+    # the dominant kernel class (per-kernel breakdown on one lane, averaged over
+    # BREAKDOWN_STEPS steps per class; fc1 and fc2 are close at DeiT-S)
     per, kt1 = {}, None
     if args.no_breakdown:
         dominant = args.kernel
     else:
-        rs.set_max_lanes(1)
-        for kname in rs.KERNELS:
-            if kname in ("score", "gather", "patch_embed", "head"):   # not launched by the encoder
-                continue
-            with rs.KernelTimer(kname) as kt:
-                for _ in range(BREAKDOWN_STEPS):
-                    enc.forward(x)
-            per[kname] = {"ms": kt.total_ms / BREAKDOWN_STEPS, "launches": kt.launches // BREAKDOWN_STEPS,
-                          "work": kt.work / BREAKDOWN_STEPS}
+        per = breakdown(enc, x, rs, BREAKDOWN_STEPS)
         dominant = max(per, key=lambda k: per[k]["ms"])
         log("per-kernel ms/step (single lane):", {k: round(v["ms"], 4) for k, v in per.items()},
             "dominant:", dominant)
-        # the dominant kernel alone on the GPU: its unshared rate, for context
-        with rs.KernelTimer(dominant) as kt1:
-            for _ in range(min(args.steps, 10)):
-                enc.forward(x)
-        rs.set_max_lanes(2)
-        torch.cuda.synchronize()
     bound = KERNEL_BOUND[dominant]
 
-    # timed region: K steps of the encoder as it runs by default (two lanes when the batch
-    # is large enough); the dominant kernel is event-timed on the stream each launch runs on
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with rs.KernelTimer(dominant) as kt:
-        start.record(stream)
-        for _ in range(args.steps):
-            enc.forward(x)
-        end.record(stream)
-        torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    value = wl.B / (ms_step / 1e3)
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step, {value:.1f} {wl.unit}/s")
+    def rate(work, ms):
+        return work / (ms / 1e3) / (1e12 if bound == "mfma" else 1e9)
 
+    # the same K steps again with the dominant kernel's launches bracketed by HIP events on
+    # the stream each launch runs on (the roofline figure); its ms/step shows what the
+    # instrumentation costs
+    with rs.KernelTimer(dominant) as kt:
+        ms_instr = time_steps(lambda: enc.forward(x), args.steps, torch)
     achieved = rate(kt.work, kt.total_ms)
     roof = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK[bound],
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(achieved / PEAK[bound], 4),
             "traffic": stored_traffic(wl.name, dominant),
             "launches_per_step": kt.launches // args.steps,
             "avg_launch_us": round(kt.total_ms * 1e3 / max(1, kt.launches), 3),
+            "work_per_launch": kt.work / max(1, kt.launches),
+            "instrumented_ms_per_step": round(ms_instr, 4),
             }
-    if kt1 is not None:
+    if not args.no_breakdown:
         # launches of the two encoder lanes overlap in the timed region; the same kernel
-        # with the batch on one stream (not timed for `value`):
+        # with the batch on one stream (its own rate):
+        prev = rs.get_max_lanes()
+        rs.set_max_lanes(1)
+        try:
+            with rs.KernelTimer(dominant) as kt1:
+                for _ in range(min(args.steps, 10)):
+                    enc.forward(x)
+        finally:
+            rs.set_max_lanes(prev)
+        torch.cuda.synchronize()
         achieved1 = rate(kt1.work, kt1.total_ms)
         roof["single_lane"] = {"achieved": round(achieved1, 2), "frac": round(achieved1 / PEAK[bound], 4),
                                "avg_launch_us": round(kt1.total_ms * 1e3 / max(1, kt1.launches), 3)}
 
-    # algorithmic flop of one step under the schedule: 2 * (12 L C^2 + 2 L^2 C) per sample-block
-    # and the token-blocks one sample passes through (tokens entering each block)
-    from_sched, token_blocks = 0.0, 0
-    L = wl.L
-    for b in range(wl.depth):
-        from_sched += 2.0 * (12 * L * wl.C ** 2 + 2 * L * L * wl.C)
-        token_blocks += L
-        if b in wl.prune_layers:
-            L = int(np.floor(wl.keep_ratios[list(wl.prune_layers).index(b)] * L + 0.5))
-    tflops = from_sched * wl.B / (ms_step / 1e3) / 1e12
+    flop, token_blocks = schedule_work(wl)
+    tflops = flop / (ms_step / 1e3) / 1e12
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": f"{wl.unit}/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02^2) weights)",
         "config": {"workload": f"{wl.name} encoder, RS pruning", "batch": wl.B, "tokens": wl.L,
                    "tokens_out": enc.L_final, "C": wl.C, "heads": wl.heads, "hidden": wl.hidden,
@@ -505,13 +615,29 @@ def main():
         line["pages_context"] = {"value": v, "unit": f"{wl.unit}/s", "source": cite,
                                  "note": "RTX A6000, whole forward pass; not the same work",
                                  "ratio": round(value / v, 2)}
-    if not (args.no_compare or args.no_breakdown):
+    context = not args.no_breakdown
+    if context and not args.no_hbm:
+        res = standalone(wl, 50)
+        line["hbm_kernels"] = {
+            "unit": "GB/s", "peak": PEAK["hbm"],
+            "note": "rs_score and rs_topk_gather alone at each prune stage's shape; algorithmic "
+                    "bytes / event time, inputs rotating over >= 512 MiB",
+            "stages": res}
+        log("standalone HBM kernels:", [(r["L"], r["score"]["frac_hbm"], r["topk_gather"]["frac_hbm"])
+                                         for r in res])
+    if context and not args.no_compare:
         line["comparison"] = compare(wl, blocks, x, args.steps, value, rs, torch)
-    if not (args.no_whole or args.no_breakdown):
+    if context and not args.no_whole:
         line["whole_forward"] = whole_forward(wl, spec, blocks, args.steps, rs, torch)
         if wl.name in PAGES_CONTEXT:
             line["pages_context"]["ratio_whole_forward"] = round(
                 line["whole_forward"]["value"] / PAGES_CONTEXT[wl.name][0], 2)
+    if context and not args.no_configs:
+        cfgs = {"deit_t_block": block_config(200, rs, torch)}
+        for name in ("deit_s", "deit_b", "umt_b", "umt_l"):
+            if name != wl.name:
+                cfgs[name] = other_config(name, 20, rs, torch)
+        line["configs"] = cfgs
     if args.copy_probe:
         copy_probe(rs, torch)
     if not args.no_cpu_baseline:

@@ -279,6 +279,8 @@ size_t rs_workspace_bytes(const rs_model_desc* desc, int depth, int B, int L);
  * launch on the caller's stream.  Process-wide; affects calls made after it returns
  * (rs_workspace_bytes covers every lane count). */
 rs_status rs_set_max_lanes(int lanes);
+/* Host only: the current most-lanes setting (what rs_set_max_lanes last stored, else 2). */
+int rs_get_max_lanes(void);
 
 /* Message for the calling thread's last failed call ("" if none); valid until the next
  * call on that thread. */

@@ -21,6 +21,9 @@ Recipe (identical for every workload unless stated):
     exercised): biases ~ N(0, 0.02^2), gamma ~ 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2);
   * ``spread=True`` multiplies each token row of x by a_i ~ U(0.5, 1.5), which
     widens the score distribution so that near-ties become rare;
+  * ``offset`` / ``spikes`` (parity tests of the folded LayerNorm): rows with a large
+    common offset and a few channels of magnitude ~50, so that |mean| / std of a row is
+    large, the regime in which LayerNorm statistics cancel;
   * bf16 workloads: values are drawn in fp32 and rounded to bf16 (round to
     nearest, ties to even) here, so the GPU path and the oracle see the very same
     numbers; arrays are returned as float32 holding bf16-representable values;
@@ -48,6 +51,7 @@ _SPREAD_TAG = 1_000_001
 _IMAGE_TAG = 1_000_002
 _EMBED_TAG = 1_000_003
 _HEAD_TAG = 1_000_004
+_SPIKE_TAG = 1_000_005
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,8 +132,14 @@ def _finish(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def make_input(wl: Workload, seed: int = 0, B: Optional[int] = None, L: Optional[int] = None,
-               spread: bool = False) -> np.ndarray:
-    """Block/encoder input x of shape [B, L, C], x ~ N(0, 1)."""
+               spread: bool = False, offset: float = 0.0, spikes: int = 0,
+               spike: float = 50.0) -> np.ndarray:
+    """Block/encoder input x of shape [B, L, C], x ~ N(0, 1).
+
+    ``offset`` adds a constant to every element (rows far from zero mean, as residual
+    streams with a large common component are); ``spikes`` picks that many channels
+    (seeded, the same for every token) and adds +-``spike`` to them, signs alternating
+    (a few large-magnitude channels)."""
     B = wl.B if B is None else B
     L = wl.L if L is None else L
     rng = np.random.default_rng([seed, _INPUT_BLOCK_TAG, 0])
@@ -137,6 +147,12 @@ def make_input(wl: Workload, seed: int = 0, B: Optional[int] = None, L: Optional
     if spread:
         a = np.random.default_rng([seed, _SPREAD_TAG, 0]).uniform(0.5, 1.5, size=(B, L, 1))
         x = x * a.astype(np.float32)
+    if offset:
+        x = x + np.float32(offset)
+    if spikes:
+        ch = np.random.default_rng([seed, _SPIKE_TAG, 0]).choice(wl.C, size=spikes, replace=False)
+        sign = np.where(np.arange(spikes) % 2 == 0, 1.0, -1.0).astype(np.float32)
+        x[..., ch] += np.float32(spike) * sign
     return _finish(x, wl.dtype)
 
 

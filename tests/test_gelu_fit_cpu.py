@@ -18,10 +18,10 @@ def _kernel_coefficients():
     body = src[src.index("float gelu_fitted(float x)"):]
     body = body[:body.index("}")]
     vals = [float(v) for v in re.findall(r"([-+]?\d\.\d+e[-+]\d+|[-+]?\d+\.\d+)f", body)]
-    # clamp bounds first (-6, 6), then the Horner constants c3, c2, c1, c0
-    assert vals[:2] == [-6.0, 6.0], vals
-    c3, c2, c1, c0 = vals[2:6]
-    return np.array([c0, c1, c2, c3], np.float32)
+    # the clamp first, then the Horner constants c4, c3, c2, c1, c0
+    assert vals[0] == gelu_fit.CLAMP, vals
+    c4, c3, c2, c1, c0 = vals[1:6]
+    return np.array([c0, c1, c2, c3, c4], np.float32)
 
 
 def test_kernel_gelu_constants_are_the_fit():
@@ -30,7 +30,13 @@ def test_kernel_gelu_constants_are_the_fit():
 
 def test_kernel_gelu_error_bound():
     c = _kernel_coefficients()
-    x = np.concatenate([np.linspace(-30, 30, 400001), [0.0, -0.0, 1e-30, -1e-30]])
+    x = np.concatenate([np.linspace(-30, 30, 400001), np.linspace(-1e4, 1e4, 200001),
+                        [0.0, -0.0, 1e-30, -1e-30]]).astype(np.float32).astype(np.float64)
     err = np.abs(gelu_fit.gelu_fitted_f32(x, c).astype(np.float64) - x * ndtr(x))
     assert err.max() <= 1.3e-5
+    # far outside: relative error negligible, no overflow of the tail term
+    big = np.array([1e6, -1e6, 1e30, -1e30, 3e38, -3e38], np.float32)
+    gb = gelu_fit.gelu_fitted_f32(big, c).astype(np.float64)
+    want = np.where(big > 0, big.astype(np.float64), 0.0)
+    assert np.all(np.abs(gb - want) <= 1e-20 * np.abs(big))
     assert gelu_fit.gelu_fitted_f32(np.array([0.0]), c)[0] == 0.0

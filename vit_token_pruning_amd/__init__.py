@@ -16,7 +16,7 @@ from ._native import BLOCK_FIELDS, KERNELS, RSError, lib  # noqa: F401
 
 __all__ = ["ModelSpec", "block_forward", "score", "topk_gather", "encoder_forward",
            "encoder_out_len", "workspace_bytes", "Encoder", "KernelTimer", "RSError", "lib",
-           "set_max_lanes", "ImageSpec", "patch_embed", "head", "ViT", "vit_forward", "attention"]
+           "set_max_lanes", "get_max_lanes", "ImageSpec", "patch_embed", "head", "ViT", "vit_forward", "attention"]
 
 _DT = {torch.float32: N.RS_F32, torch.bfloat16: N.RS_BF16}
 # representation shift variants of the ablations and the attention-map baselines
@@ -351,6 +351,11 @@ def set_max_lanes(lanes: int) -> None:
     """Most concurrent lanes (streams) the encoder may split a batch into: 1 .. 4
     (default 2)."""
     N.check("rs_set_max_lanes", lib().rs_set_max_lanes(int(lanes)))
+
+
+def get_max_lanes() -> int:
+    """The current most-lanes setting of the encoder (see set_max_lanes)."""
+    return int(lib().rs_get_max_lanes())
 
 
 class KernelTimer:

@@ -100,6 +100,7 @@ def lib():
         "rs_workspace_bytes": (c_size_t, [P_DESC, c_int, c_int, c_int]),
         "rs_last_error": (ctypes.c_char_p, []),
         "rs_set_max_lanes": (c_int, [c_int]),
+        "rs_get_max_lanes": (c_int, []),
         "rs_timing_begin": (c_int, [c_int]),
         "rs_timing_end": (c_int, [ctypes.POINTER(c_float), P_INT, P_DBL]),
     }

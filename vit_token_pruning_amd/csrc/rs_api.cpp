@@ -395,6 +395,7 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
     ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
+    ep.stats_in = st_x;   // x's row means: fc1's operand is stored as (x' - mean(x)) * gamma2
     ep.split_ws = ws.split;
     if (part && d.score_op == RS_SHIFT_ATTN) set_score(ep, d, part);   // D(p, x)
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
@@ -836,17 +837,15 @@ size_t rs_attention_workspace_bytes(const rs_model_desc* desc, int B, int L) {
   return up256(bhl * 4) + up256(bhl * ((L + 63) / 64) * 4);
 }
 
-rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
-                       void* map, float* score_cls, float* score_mean, void* workspace,
-                       size_t ws_bytes, hipStream_t stream) {
-  rs_status s;
-  if ((s = check_desc(desc)) != RS_OK) return s;
-  if ((s = check_BL(B, L, desc->C, 3 * desc->C)) != RS_OK) return s;
-  if ((s = check_ptr(qkv, "qkv")) != RS_OK) return s;
-  if ((s = check_ptr(out, "out")) != RS_OK) return s;
-  if (map && (s = check_ptr(map, "map")) != RS_OK) return s;
-  if (score_cls && (s = check_ptr(score_cls, "score_cls", 4)) != RS_OK) return s;
-  if (score_mean && (s = check_ptr(score_mean, "score_mean", 4)) != RS_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// rs_attention after its pointer checks, with the scratch of the score sums at `ws`
+// (ws_bytes available; none needed when no score is asked).
+rs_status run_attention(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
+                        void* map, float* score_cls, float* score_mean, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   const rs::Dtype dt = dtype_of(*desc);
   const double flop = 4.0 * B * (double)L * L * desc->C;
   const size_t bhl = (size_t)B * desc->heads * L;
@@ -858,12 +857,11 @@ rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L,
   }
   float *cls = nullptr, *colsum = nullptr;
   if (score_cls || score_mean) {
-    if ((s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
     if (ws_bytes < rs_attention_workspace_bytes(desc, B, L))
       return fail(RS_ERR_WORKSPACE, "workspace too small: need " +
                                         std::to_string(rs_attention_workspace_bytes(desc, B, L)) + " bytes");
-    if (score_cls) cls = static_cast<float*>(workspace);
-    if (score_mean) colsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + up256(bhl * 4));
+    if (score_cls) cls = static_cast<float*>(ws);
+    if (score_mean) colsum = reinterpret_cast<float*>(static_cast<char*>(ws) + up256(bhl * 4));
   }
   RS_HIP(timed(RS_KERNEL_ATTENTION, flop, stream, [&] {
     return rs::launch_attention_map(dt, qkv, out, B, L, desc->heads, map, rs::map_pad(L), cls,
@@ -878,6 +876,32 @@ rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L,
       return rs::launch_map_scores(nullptr, colsum, B, L, desc->heads, 1, score_mean, stream);
     }));
   return RS_OK;
+}
+
+rs_status check_attention(const rs_model_desc* desc, const void* qkv, int B, int L, const void* out,
+                          const void* map, const float* score_cls, const float* score_mean) {
+  rs_status s;
+  if ((s = check_desc(desc)) != RS_OK) return s;
+  if ((s = check_BL(B, L, desc->C, 3 * desc->C)) != RS_OK) return s;
+  if ((s = check_ptr(qkv, "qkv")) != RS_OK) return s;
+  if ((s = check_ptr(out, "out")) != RS_OK) return s;
+  if (map && (s = check_ptr(map, "map")) != RS_OK) return s;
+  if (score_cls && (s = check_ptr(score_cls, "score_cls", 4)) != RS_OK) return s;
+  if (score_mean && (s = check_ptr(score_mean, "score_mean", 4)) != RS_OK) return s;
+  return RS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
+                       void* map, float* score_cls, float* score_mean, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_attention(desc, qkv, B, L, out, map, score_cls, score_mean)) != RS_OK) return s;
+  if ((score_cls || score_mean) && (s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
+  return run_attention(desc, qkv, B, L, out, map, score_cls, score_mean, workspace, ws_bytes, stream);
 }
 
 rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C, int dtype,
@@ -1034,6 +1058,8 @@ rs_status rs_set_max_lanes(int lanes) {
   g_max_lanes.store(lanes);
   return RS_OK;
 }
+
+int rs_get_max_lanes(void) { return g_max_lanes.load(); }
 
 rs_status rs_timing_begin(int kernel_id) {
   if (kernel_id < 0 || kernel_id >= RS_KERNEL_COUNT) return fail(RS_ERR_INVALID_ARG, "bad kernel id");

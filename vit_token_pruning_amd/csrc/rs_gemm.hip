@@ -9,9 +9,10 @@
 // d = W beta + b.  LayerNorm 1: the GEMM consumes the raw block input z = x against
 // W' = W diag(gamma) (c = W' 1), prepared per call with c and d (rs_rowops.hip,
 // fold_kernel).  LayerNorm 2: the projection epilogue, which forms x' in fp32, stores
-// x' * gamma for fc1 (one rounding, as a LayerNorm output would have), and fc1 uses its
-// own weights.  Row statistics arrive as per-64-column slice partials from the kernel
-// that produced the rows.
+// (x' - a) * gamma for fc1, a = the row mean of the block input (one rounding of a value
+// near zero mean, as a LayerNorm output would have, even for rows far from zero mean;
+// the shift does not change LN(x')), and fc1 uses its own weights.  Row statistics arrive
+// as per-64-column slice partials from the kernel that produced the rows.
 //
 // The score is Eq. (4) of "Representation Shift: Unifying Token Compression with
 // FlashAttention" (arXiv HTML), Sec. 3.2, for the MLP sublayer of Sec. 3.3 (case ii)
@@ -38,18 +39,21 @@
 namespace rs {
 namespace {
 
-// GELU for bf16 outputs: x * Phi(x) with Phi(x) = logistic(t * P(t^2)), t = clamp(x, +-6),
-// P a degree-3 polynomial in t^2 fitted (weighted minimax) to the logit of the normal
-// CDF, log2(e) folded in so the logistic is 1 / (1 + 2^-(t P)).  Max |error| against the
-// exact erf form over all x: 1.3e-5 (about 1/150 of a bf16 half-ulp at 1).
+// GELU for bf16 outputs.  With Q(t) = 1 - Phi(t) the upper normal tail, Phi(x) = 1 - Q(x)
+// for x >= 0 and Q(-x) otherwise, so x Phi(x) = max(x, 0) - |x| Q(|x|) for every x.  Q is
+// evaluated as 2^R(t), R a degree-4 polynomial in t = min(|x|, 13) fitted (weighted minimax)
+// to log2 Q on [0, 5.5] (beyond, R keeps falling below -25, so the tail term is < 3e-8 |x|):
+// one hardware exp2 and no reciprocal.  Max |error| against the exact erf form for finite
+// inputs: 6.2e-6 (|x| < 1e4; relative error < 1e-24 beyond).  +-Inf inputs give NaN.
 __device__ __forceinline__ float gelu_fitted(float x) {
-  const float t = __builtin_amdgcn_fmed3f(x, -6.0f, 6.0f);
-  const float u = t * t;
-  float p = fmaf(u, -2.4996252250275575e-05f, -7.343353936448693e-04f);
-  p = fmaf(p, u, 1.059778556227684e-01f);
-  p = fmaf(p, u, 2.3016505241394043f);
-  const float e = __builtin_amdgcn_exp2f(-(t * p));
-  return x * __builtin_amdgcn_rcpf(1.0f + e);
+  const float ax = fabsf(x);
+  const float t = fminf(ax, 13.0f);
+  float p = fmaf(t, 3.865753533318639e-03f, -4.4075679033994675e-02f);
+  p = fmaf(p, t, -4.6802330017089844e-01f);
+  p = fmaf(p, t, -1.1473647356033325f);
+  p = fmaf(p, t, -1.0004818439483643f);
+  const float q = __builtin_amdgcn_exp2f(p);
+  return fmaf(-ax, q, fmaxf(x, 0.0f));
 }
 template <typename T> __device__ __forceinline__ float gelu_t(float x);
 template <> __device__ __forceinline__ float gelu_t<bf16>(float x) { return gelu_fitted(x); }
@@ -139,6 +143,18 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
         rpart[q] = *reinterpret_cast<const float2*>(ep.stats_in + ((size_t)m * sstride + q) * 2);
     }
   }
+  // kEpiProj: thread t < 128 fetches the slice means of the block input's row t (x's
+  // statistics, when given): its row mean, subtracted from x' before x' * gamma2 is stored
+  float rmean[16];
+  const bool kShift = EPI == kEpiProj && ep.stats_in != nullptr;
+  if (kShift && tid < G::BM) {
+    const int m = m0 + tid;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      rmean[q] = 0.f;
+      if (q < nsl && m < M) rmean[q] = ep.stats_in[((size_t)m * sstride + q) * 2];
+    }
+  }
   Frag8<T> px[NPASS], pp[NPASS];           // kResid: x (and p) of each row; kPatch: pos
   if (kResid || kPatch) {
 #pragma unroll
@@ -176,7 +192,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
     float mean = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) mean += rpart[q].x;  // absent slices hold 0
-    mean /= (float)nsl;
+    mean *= __builtin_amdgcn_rcpf((float)nsl);
     float m2 = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q)
@@ -184,8 +200,15 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
         const float dm = rpart[q].x - mean;
         m2 += rpart[q].y + 64.f * dm * dm;
       }
-    const float rstd = 1.0f / sqrtf(m2 / (float)ep.C + ep.eps);
+    // hardware reciprocal and reciprocal square root (about 1 ulp each)
+    const float rstd = __builtin_amdgcn_rsqf(fmaf(m2, __builtin_amdgcn_rcpf((float)ep.C), ep.eps));
     Rs[tid] = make_float2(mean * rstd, rstd);
+  }
+  if (kShift && tid < G::BM) {
+    float mean = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mean += rmean[q];  // absent slices hold 0
+    Rs[tid] = make_float2(mean * __builtin_amdgcn_rcpf((float)nsl), 0.f);
   }
 
   // row pass: 8 consecutive columns per thread; lanes 0-7 / 8-15 of a row cover its two
@@ -245,13 +268,19 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
         for (int e = 0; e < 8; ++e) w[e] = round_t<T>(v[e] + b8[e] + xv[e]);   // + pos
         store8f(out + orow * ep.ldo + n, w);
       } else if (EPI == kEpiProj) {
+        // LayerNorm is invariant to a shift of its row, so fc1's operand and LayerNorm 2's
+        // statistics are taken of x' - a, a = the row mean of the block input x (0 when its
+        // statistics are not given).  x' - a is near zero mean even for rows far from
+        // zero mean, so storing (x' - a) * gamma2 in the storage type keeps its precision
+        // relative to the row's spread, as storing the normalised row would.
+        const float a = kShift ? Rs[mm].x : 0.f;
         float u[8], pf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pf[e] = v[e] + b8[e];               // attention branch SA(LN(x)) in fp32
           pv[e] = round_t<T>(pf[e]);          // ... as stored
-          w[e] = xv[e] + pv[e];               // x' (Eq. 5) in fp32: LayerNorm 2 statistics
-          u[e] = w[e] * g8[e];                // x' * gamma2: fc1's A operand
+          w[e] = (xv[e] - a) + pv[e];         // x' (Eq. 5) - a in fp32: LayerNorm 2 statistics
+          u[e] = w[e] * g8[e];                // (x' - a) * gamma2: fc1's A operand
         }
         store8f(out + (size_t)m * ep.ldo + n, pv);
         store8f(static_cast<T*>(ep.out2) + (size_t)m * N + n, u);

@@ -26,7 +26,8 @@ __host__ __device__ inline int stat_stride(int C) { return (C / 64 + 1) / 2 * 2;
 
 enum GemmEpilogue {
   kEpiQKV = 0,   // LN1 folded; Q|K|V -> qkv [M][3C]
-  kEpiProj = 1,  // p = acc + b -> out; x' = x + p -> out2; LN2 slice partials of x' -> stats_out
+  kEpiProj = 1,  // p = acc + b -> out; (x' - a) * gamma2 -> out2 with x' = x + p and a the
+                 // row mean of x (from stats_in; 0 if null); LN2 slice partials of x' - a
   kEpiGelu = 2,  // LN2 folded, GELU -> out [M][N]                 (fc1)
   kEpiFc2 = 3,   // y = acc + b2; out = (x + p) + y; score partials; LN1 slice partials of out
   kEpiPatch = 4, // patch embedding: A gathered from images; out row = acc + b + pos, placed
