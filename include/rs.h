@@ -148,6 +148,22 @@ rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L,
                        size_t ws_bytes, hipStream_t stream);
 size_t rs_attention_workspace_bytes(const rs_model_desc* desc, int B, int L);
 
+/* rs_attention without a workspace, for callers that cannot allocate device memory
+ * (work under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, validation and results as rs_attention; the score sums live in a
+ * fixed scratch array of RS_NOALLOC_SCRATCH_BYTES inside the library, one per device
+ * (held from the library's first use on that device until the process ends).  No call
+ * allocates or frees memory.  A call that asks for a score whose sums exceed the limit
+ * (rs_attention_workspace_bytes(desc, B, L) > RS_NOALLOC_SCRATCH_BYTES) returns
+ * RS_ERR_UNSUPPORTED and enqueues nothing.  Every call on one device shares that array
+ * and fully overwrites the part it uses: calls whose work may overlap in time on the same
+ * device (concurrent streams, or host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. */
+#define RS_NOALLOC_SCRATCH_BYTES (16u << 20)
+rs_status rs_attention_noalloc(const rs_model_desc* desc, const void* qkv, int B, int L,
+                               void* out, void* map, float* score_cls, float* score_mean,
+                               hipStream_t stream);
+
 /* Per-sample selection and compaction: keep the keep_k highest scores of each sample
  * (ties to the lower index, NaN lowest, token 0 always kept if has_cls), write their
  * indices ascending to kept_idx [B][keep_k] and, if x_kept is not null, the rows

@@ -260,3 +260,19 @@ def test_patch_embed_head_and_forward_validation(N):
     assert fw(sched=(N.int_array([3, 3]), N.dbl_array([0.7, 0.7]), 2)) == E_ARG
     assert fw(h=N.HeadWeights(FAKE, FAKE, FAKE, FAKE, 12, N.RS_POOL_CLS)) == E_UNS
     assert fw(img=N.ImageDesc(1, 3, 224, 224, 12)) == E_UNS
+
+
+def test_attention_noalloc_validation(N):
+    """rs_attention_noalloc validates like rs_attention and rejects, before any HIP call, a
+    score whose sums exceed the library's fixed scratch (16 MiB)."""
+    lib = N.lib()
+    d = _desc(N, C=768, heads=12, hidden=3072, has_cls=0)
+    # Eq. (3) column sums of 20 clips x 2352 tokens x 12 heads x 37 query blocks: ~84 MB
+    st = lib.rs_attention_noalloc(ctypes.byref(d), FAKE, 20, 2352, FAKE, None, None, FAKE, None)
+    assert st == N.RS_ERR_UNSUPPORTED
+    assert b"scratch" in lib.rs_last_error()
+    assert lib.rs_attention_workspace_bytes(ctypes.byref(d), 20, 2352) > (16 << 20)
+    # the usual argument checks come first
+    assert lib.rs_attention_noalloc(ctypes.byref(d), None, 2, 197, FAKE, None, None, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_attention_noalloc(ctypes.byref(d), FAKE, 2, 197, FAKE + 4, None, None, None, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_attention_noalloc(ctypes.byref(d), FAKE, 0, 197, FAKE, None, None, None, None) == N.RS_ERR_INVALID_ARG

@@ -89,6 +89,8 @@ def lib():
         "rs_attention": (c_int, [P_DESC, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
         "rs_attention_workspace_bytes": (c_size_t, [P_DESC, c_int, c_int]),
+        "rs_attention_noalloc": (c_int, [P_DESC, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
         "rs_patch_embed": (c_int, [P_DESC, P_IMG, P_EMB, c_void_p, c_int, c_void_p, c_void_p]),
         "rs_head": (c_int, [P_DESC, P_HEAD, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
                             c_size_t, c_void_p]),

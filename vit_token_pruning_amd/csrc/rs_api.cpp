@@ -18,6 +18,9 @@
 #include "../../include/rs.h"
 #include "rs_launch.hpp"
 
+static_assert(RS_NOALLOC_SCRATCH_BYTES == rs::kNoallocScratchBytes,
+              "the header's scratch limit must match the library's array");
+
 namespace {
 
 thread_local std::string g_err;
@@ -902,6 +905,25 @@ rs_status rs_attention(const rs_model_desc* desc, const void* qkv, int B, int L,
   if ((s = check_attention(desc, qkv, B, L, out, map, score_cls, score_mean)) != RS_OK) return s;
   if ((score_cls || score_mean) && (s = check_ptr(workspace, "workspace", 256)) != RS_OK) return s;
   return run_attention(desc, qkv, B, L, out, map, score_cls, score_mean, workspace, ws_bytes, stream);
+}
+
+rs_status rs_attention_noalloc(const rs_model_desc* desc, const void* qkv, int B, int L, void* out,
+                               void* map, float* score_cls, float* score_mean, hipStream_t stream) {
+  rs_status s;
+  if ((s = check_attention(desc, qkv, B, L, out, map, score_cls, score_mean)) != RS_OK) return s;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (score_cls || score_mean) {
+    const size_t need = rs_attention_workspace_bytes(desc, B, L);
+    if (need > rs::kNoallocScratchBytes)
+      return fail(RS_ERR_UNSUPPORTED, "the score sums need " + std::to_string(need) +
+                                          " bytes of scratch, more than the library's fixed " +
+                                          std::to_string(rs::kNoallocScratchBytes) +
+                                          " (use rs_attention with a workspace)");
+    RS_HIP(rs::noalloc_scratch(&ws));
+    ws_bytes = rs::kNoallocScratchBytes;
+  }
+  return run_attention(desc, qkv, B, L, out, map, score_cls, score_mean, ws, ws_bytes, stream);
 }
 
 rs_status rs_topk_gather(const float* scores, const void* x, int B, int L, int C, int dtype,

@@ -195,4 +195,10 @@ inline int topk_copy_split(int B) {
 // ids[b][i] = i
 hipError_t launch_iota(int32_t* ids, int B, int L, hipStream_t stream);
 
+// Scratch of the entry points that allocate nothing: a device array of this many bytes
+// in the library's code object, one per device.  noalloc_scratch() returns the current
+// device's copy (its address is looked up once per device and kept).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace rs
