@@ -109,3 +109,45 @@ def test_score_matches_oracle(dt, B, L, C):
     # good to ~C * 2^-24, so anything above 1e-4 would indicate a defect
     assert rel.max() <= 1e-4
     assert rs.score(torch.zeros(2, 3, 64, device="cuda"), torch.zeros(2, 3, 64, device="cuda")).abs().max() == 0
+
+
+# Boundaries of the one-wave selection (4 / 8 / 16 / 32 keys per lane up to 2048 tokens,
+# the workgroup path beyond) and score sets that stress the radix passes: every competing
+# score equal (no bit to resolve), two distinct values, scores spread over the whole float
+# range (keys differing in the top bit), and many NaNs.
+BOUNDS = [(3, 256, 100, True), (3, 257, 100, False), (2, 512, 511, True), (2, 513, 2, False),
+          (2, 1024, 1023, False), (2, 1025, 700, True), (2, 2048, 1024, False),
+          (2, 2049, 1024, True), (4, 1568, 1, True), (4, 1568, 1568, False)]
+
+
+@pytest.mark.parametrize("B,L,k,cls", BOUNDS)
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed"])
+def test_topk_gather_wave_boundaries(B, L, k, cls, kind):
+    _run(B, L, k, cls, kind, seed=5 * L + k + B)
+
+
+@pytest.mark.parametrize("L,k,cls", [(197, 138, True), (1568, 784, False), (700, 350, True)])
+@pytest.mark.parametrize("pattern", ["equal", "two", "wide", "nans"])
+def test_topk_gather_degenerate_scores(L, k, cls, pattern):
+    import torch
+    import vit_token_pruning_amd as rs
+    B = 3
+    rng = np.random.default_rng([L, k, len(pattern)])
+    if pattern == "equal":
+        s = np.full((B, L), 7.25, np.float32)
+    elif pattern == "two":
+        s = np.where(rng.random((B, L)) < 0.5, 3.0, 5.0).astype(np.float32)
+    elif pattern == "wide":
+        s = (np.sign(rng.standard_normal((B, L))) *
+             np.exp2(rng.uniform(-120, 120, (B, L)))).astype(np.float32)
+    else:
+        s = rng.standard_normal((B, L)).astype(np.float32)
+        s[rng.random((B, L)) < 0.3] = np.nan
+    x = synth.round_to_bf16(rng.standard_normal((B, L, 64)).astype(np.float32))
+    kept, xk = rs.topk_gather(torch.from_numpy(s).cuda(), torch.from_numpy(x).cuda().to(torch.bfloat16), k, cls)
+    torch.cuda.synchronize()
+    kept, xk = kept.cpu().numpy(), xk.float().cpu().numpy()
+    for b in range(B):
+        want = O.select_kept(s[b], k, cls)
+        assert kept[b].tolist() == want, f"sample {b}"
+        np.testing.assert_array_equal(xk[b], x[b][want])

@@ -183,10 +183,11 @@ hipError_t launch_topk(const float* scores, const float* part, int P, int dist, 
 // partial quantities per slice of each distance (cosine: a.b, a.a, b.b)
 inline int dist_quantities(int dist) { return dist == 2 ? 3 : 1; }
 // With row sets to copy, the top-k launch runs topk_copy_split(B) workgroups per sample:
-// each makes the same selection and copies its share of the kept rows, so that small
-// batches still spread the copy over about kTopkTargetWgs workgroups (the selection is a
-// few passes over one sample's L keys in LDS; the copy is what needs the bandwidth).
-constexpr int kTopkTargetWgs = 128, kTopkMaxSplit = 64;
+// each makes the same selection and copies its share of the kept rows, so that every batch
+// size spreads the copy over about kTopkTargetWgs workgroups (two per CU: one workgroup's
+// selection overlaps another's copy; the selection is a few passes over one sample's L
+// keys, the copy is what needs the bandwidth).
+constexpr int kTopkTargetWgs = 512, kTopkMaxSplit = 128;
 inline int topk_copy_split(int B) {
   const int g = (kTopkTargetWgs + B - 1) / B;
   return g < 1 ? 1 : (g > kTopkMaxSplit ? kTopkMaxSplit : g);

@@ -260,26 +260,27 @@ __device__ __forceinline__ float finish_dist(int dist, float s0, float s1, float
   return 1.0f - s0 / fmaxf(sqrtf(s1) * sqrtf(s2), 1e-8f);
 }
 
-// 16 lanes per row: D(fx, x) accumulated in fp32.
-template <typename T>
+// LPR lanes per row: D(fx, x) accumulated in fp32.
+template <typename T, int LPR>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
                                                     const T* __restrict__ x,
                                                     float* __restrict__ s, int M, int C,
                                                     int dist) {
-  // 16 lanes per row; each lane takes every 16th 8-element chunk.  A row of up to 1024
-  // elements is at most 8 chunks per lane, all requested before any is used, so a lane
-  // waits for memory once per 8 chunks instead of once per chunk.
+  // LPR lanes per row (8 for rows of up to 64 chunks, else 16); each lane takes every
+  // LPR-th 8-element chunk, so a row is at most 8 chunks per lane, all requested before
+  // any is used: a lane waits for memory once per 8 chunks instead of once per chunk, and
+  // short rows still keep 6-8 chunks per lane in flight.
   constexpr int U = 8;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
+  const int row = blockIdx.x * (256 / LPR) + (threadIdx.x / LPR), sub = threadIdx.x % LPR;
   float s0 = 0.f, s1 = 0.f, s2 = 0.f;
   if (row < M) {
     const size_t base = (size_t)row * C;
     const int nch = C >> 3;
-    for (int c0 = 0; c0 < nch; c0 += 16 * U) {
+    for (int c0 = 0; c0 < nch; c0 += LPR * U) {
       Frag8<T> fa[U], fb[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ch = c0 + sub + 16 * u;
+        const int ch = c0 + sub + LPR * u;
         if (ch < nch) {
           load_frag(fa[u], fx + base + ch * 8);
           load_frag(fb[u], x + base + ch * 8);
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ch = c0 + sub + 16 * u;
+        const int ch = c0 + sub + LPR * u;
         if (ch < nch) {
           float a[8], b[8];
           frag_to_f32(fa[u], a);
@@ -313,10 +314,18 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ fx,
       }
     }
   }
-  s0 = sum16(s0);
-  if (dist == 2) {
-    s1 = sum16(s1);
-    s2 = sum16(s2);
+  if (LPR == 8) {
+    s0 = sum8(s0);
+    if (dist == 2) {
+      s1 = sum8(s1);
+      s2 = sum8(s2);
+    }
+  } else {
+    s0 = sum16(s0);
+    if (dist == 2) {
+      s1 = sum16(s1);
+      s2 = sum16(s2);
+    }
   }
   if (sub == 0 && row < M) s[row] = finish_dist(dist, s0, s1, s2);
 }
@@ -332,29 +341,47 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 1024;
-constexpr int kWaveMaxL = 256;
+constexpr int kTopkThreads = 512, kTopkWaves = kTopkThreads / 64;
+// Radix select: 11-bit digits (at most three passes over a 32-bit key), each pass with its
+// own histogram of 2048 bins plus 64 buckets of 32 bins (the bucket counts let a wave find
+// the selected bin with two 64-lane scans instead of reading all 2048 bins).
+constexpr int kDigitBits = 11, kBins = 1 << kDigitBits, kBuckets = kBins / 32, kPasses = 3;
+static_assert(32 * kTopkThreads >= RS_MAX_TOKENS, "top-k holds at most 32 keys per thread");
+static_assert(RS_MAX_TOKENS < 65536, "the emission scan packs two 16-bit counts");
 
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+// Wave-wide inclusive scans with DPP: row shifts by 1, 2, 4, 8 within each row of 16
+// lanes, then row 0's total broadcast into row 1 (and row 2's into row 3), then lane 31's
+// into rows 2 and 3.  Lanes a shift leaves without a source take `id`.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));
   return v;
 }
-
-// exclusive prefix sum over the 1024 threads of the workgroup
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MinU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) { return wave_scan(v, 0u, AddU32()); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(v, ~0u, MinU32()), 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(v, 0u, MaxU32()), 63);
+}
+// exclusive prefix sum over the threads of the workgroup (kTopkWaves waves)
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = (int)wave_inclusive_scan((uint32_t)v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -363,19 +390,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return before + incl - v;
 }
 
-// One workgroup per sample, or G per sample when rows are copied (see below).  Selection
-// of the k largest keys (ties to the lower index): the
-// exact k-th largest key T by a 4-pass 8-bit radix select (MSB first) over an LDS
-// histogram; kept = every key above T plus the lowest-index keys equal to it.
-//  - L <= kWaveMaxL: wave 0 alone, 4 keys per lane, lane scans instead of workgroup
-//    barriers (a short row's selection is otherwise all barrier latency).
-//  - longer L: all threads, one histogram pass per 8 bits with workgroup barriers.
-// Kept indices are emitted in ascending index order (block scans), composed with ids_in,
-// and listed in LDS; then the workgroup copies up to two row sets of the kept rows
-// (RowCopy: 16-byte units per row), so selection and compaction are one launch.  With G
-// workgroups per sample every one of them makes the (deterministic, integer-only)
-// selection, copies its contiguous share of the kept rows, and only the first writes the
-// scores, indices and ids.
+// Rows of kept tokens to copy (16-byte units per row).
 struct RowCopy {
   const char* src;  // [L] rows of `units` 16-byte units per sample, or null
   char* dst;        // [k] rows per sample
@@ -417,194 +432,184 @@ __device__ __forceinline__ void copy_rows(const RowCopy& c, const uint32_t* list
   }
 }
 
+// LDS of the top-k kernel: per radix pass the bin counts and the 32-bin bucket counts
+// (cleared once, so a pass never waits for the previous pass's readers), per-wave partials.
+struct __attribute__((aligned(16))) TopkShared {
+  uint32_t fine[kPasses][kBins];
+  uint32_t coarse[kPasses][kBuckets];
+  uint32_t wlo[kTopkWaves], whi[kTopkWaves];
+  int wsum[kTopkWaves];
+};
+
+// One workgroup per sample, or G per sample when rows are copied.  Thread t holds the
+// keys of tokens t R .. t R + R - 1 in registers (R = keys per thread, L <= R kTopkThreads).
+// The score of each token is finished from the GEMM epilogues' partials (or read) and
+// mapped to an order key; the class token (index 0 when has_cls) is kept outside the
+// selection.  Selection of the k largest (ties to the lower index): the competing keys'
+// common high bits are skipped (their minimum and maximum share them), then MSB-first
+// 11-bit digits: each pass counts the keys that match the prefix found so far into its
+// histogram, one workgroup barrier, and every wave finds the same bin holding the
+// krem-th largest (bucket scan, then bin scan).  T = the k-th largest key, krem = how
+// many of its copies are kept (the lowest-index ones); a bin whose keys are all kept ends
+// the passes early (T = the bin's lowest possible key, every copy kept).  One packed scan
+// of (keys above T, keys equal to T) per thread places the kept tokens in ascending index
+// order.  With G workgroups per sample every one of them makes the same (integer-only)
+// selection and copies its contiguous share of the kept rows (listed in dynamic LDS);
+// workgroup 0 of the sample alone writes the scores, indices and ids.
+template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, const float* __restrict__ part, int P, int dist, int L,
     int k, int has_cls, float* __restrict__ scores_out, int32_t* __restrict__ kept,
     const int32_t* __restrict__ ids_in, int32_t* __restrict__ ids_out, RowCopy c0, RowCopy c1,
     int G) {
-  __shared__ __attribute__((aligned(16))) uint32_t keys[RS_MAX_TOKENS];  // keys, then the kept list
-  __shared__ uint32_t hist[256];
-  __shared__ int wsum[kTopkThreads / 64];
-  __shared__ uint32_t sel[2];
-  // G workgroups per sample: each makes the same selection; workgroup g copies kept rows
-  // [g k / G, (g + 1) k / G), and workgroup 0 alone writes scores, indices and ids
+  __shared__ TopkShared sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t list[];   // k words when copying
   const int b = blockIdx.x / G, g = blockIdx.x - b * G, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const bool lead = g == 0;
-  const int cj0 = (int)((long long)g * k / G), cj1 = (int)((long long)(g + 1) * k / G);
   const size_t rb = (size_t)b * L;
-
-  for (int i = tid; i < L; i += kTopkThreads) {
-    float s;
-    if (part) {
-      // the token's slice partials: quantity q of slice p at q * P + p
-      const float* pp = part + (rb + i) * (size_t)(dist == 2 ? 3 * P : P);
-      float a = 0.f, aa = 0.f, bb = 0.f;
-      for (int q = 0; q < P; ++q) a += pp[q];
-      if (dist == 2)
-        for (int q = 0; q < P; ++q) {
-          aa += pp[P + q];
-          bb += pp[2 * P + q];
-        }
-      s = finish_dist(dist, a, aa, bb);
-    } else {
-      s = scores[rb + i];
-    }
-    if (scores_out && lead) scores_out[rb + i] = s;
-    keys[i] = (has_cls && i == 0) ? 0xFFFFFFFFu : order_key(s);
-  }
-  __syncthreads();
-
-  // per-thread segment [i0, i1) and its keep flags (bit i - i0)
-  const int seg = (L + kTopkThreads - 1) / kTopkThreads;  // <= 16
-  const int i0 = min(tid * seg, L), i1 = min(i0 + seg, L);
-  uint32_t keepbits = 0u;
-  if (L <= kWaveMaxL) {
-    // wave 0 alone: lane l holds keys 4l .. 4l + 3
-    if (tid < 64) {
-      const int lane = tid;
-      uint32_t kk[4];
-      bool valid[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        valid[q] = 4 * lane + q < L;
-        kk[q] = valid[q] ? keys[4 * lane + q] : 0u;
-      }
-      uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (valid[q] && (kk[q] & pmask) == prefix) atomicAdd(&hist[(kk[q] >> shift) & 255u], 1u);
-        __builtin_amdgcn_wave_barrier();
-        // lane covers bins 255-4*lane down to 252-4*lane; counts above run high -> low
-        uint32_t c[4], loc = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c[q] = hist[255 - 4 * lane - q];
-          loc += c[q];
-        }
-        uint32_t above = wave_inclusive_scan(loc) - loc;
-        uint32_t bin = 0u, ab = 0u;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (above < krem && above + c[q] >= krem) {
-            found = true;
-            bin = (uint32_t)(255 - 4 * lane - q);
-            ab = above;
-          }
-          above += c[q];
-        }
-        const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
-        bin = __shfl(bin, src, 64);
-        ab = __shfl(ab, src, 64);
-        prefix |= bin << shift;
-        pmask |= 0xFFu << shift;
-        krem -= ab;
-        __builtin_amdgcn_wave_barrier();
-      }
-      const uint32_t T = prefix;  // the k-th largest key; krem of its copies are kept
-      uint32_t eq = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) eq += (valid[q] && kk[q] == T) ? 1u : 0u;
-      uint32_t e = wave_inclusive_scan(eq) - eq;
-      uint32_t keep = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (valid[q] && (kk[q] > T || (kk[q] == T && e < krem))) keep |= 1u << q;
-        e += (valid[q] && kk[q] == T) ? 1u : 0u;
-      }
-      const uint32_t cnt = __builtin_popcount(keep);
-      uint32_t pos = wave_inclusive_scan(cnt) - cnt;
-      int32_t* kb = kept + (size_t)b * k;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (((keep >> q) & 1u) && pos < (uint32_t)k) {
-          const int i = 4 * lane + q;
-          if (lead) {
-            kb[pos] = i;
-            if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
-          }
-          keys[pos] = (uint32_t)i;  // kept list (the keys were read into registers above)
-          ++pos;
-        }
-      }
-    }
-    if (!c0.src && !c1.src) return;
-    __syncthreads();
-    copy_rows(c0, keys, b, L, k, cj0, cj1);
-    copy_rows(c1, keys, b, L, k, cj0, cj1);
-    return;
-  }
   {
-    uint32_t prefix = 0u, pmask = 0u;
-    uint32_t krem = (uint32_t)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();
-      for (int i = tid; i < L; i += kTopkThreads) {
-        const uint32_t key = keys[i];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane covers bins 255-4*tid down to 252-4*tid; counts above run high -> low
-        uint32_t c[4], loc = 0u;
+    constexpr int n4 = kPasses * (kBins + kBuckets) / 4;   // fine and coarse are contiguous
+    u32x4* h = reinterpret_cast<u32x4*>(&sh.fine[0][0]);
+    for (int i = tid; i < n4; i += kTopkThreads) h[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  const int i0 = tid * R;
+  float sv[R];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c[q] = hist[255 - 4 * tid - q];
-          loc += c[q];
-        }
-        uint32_t incl = loc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t t = __shfl_up(incl, o, 64);
-          if (tid >= o) incl += t;
-        }
-        uint32_t above = incl - loc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (above < krem && above + c[q] >= krem) {
-            sel[0] = (uint32_t)(255 - 4 * tid - q);
-            sel[1] = above;
+  for (int j = 0; j < R; ++j) {
+    const int i = i0 + j;
+    sv[j] = 0.f;
+    if (i < L) {
+      if (part) {
+        // the token's slice partials: quantity q of slice p at q * P + p
+        const float* pp = part + (rb + i) * (size_t)(dist == 2 ? 3 * P : P);
+        float a = 0.f, aa = 0.f, bb = 0.f;
+        for (int q = 0; q < P; ++q) a += pp[q];
+        if (dist == 2)
+          for (int q = 0; q < P; ++q) {
+            aa += pp[P + q];
+            bb += pp[2 * P + q];
           }
-          above += c[q];
-        }
+        sv[j] = finish_dist(dist, a, aa, bb);
+      } else {
+        sv[j] = scores[rb + i];
       }
-      __syncthreads();
-      prefix |= sel[0] << shift;
-      pmask |= 0xFFu << shift;
-      krem -= sel[1];
-      __syncthreads();
-    }
-    const uint32_t T = prefix;  // the k-th largest key; krem of its copies are kept
-    int eq = 0;
-    for (int i = i0; i < i1; ++i) eq += keys[i] == T;
-    int e = block_exclusive_scan(eq, wsum);
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t key = keys[i];
-      if (key > T || (key == T && (uint32_t)e < krem)) keepbits |= 1u << (i - i0);
-      e += key == T;
     }
   }
-  int pos = block_exclusive_scan(__builtin_popcount(keepbits), wsum);  // also orders keys reads
+  uint32_t kk[R];
+  uint32_t vmask = 0u, lo = ~0u, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = i0 + j;
+    kk[j] = order_key(sv[j]);
+    if (i < L) {
+      if (scores_out && lead) scores_out[rb + i] = sv[j];
+      if (!(has_cls && i == 0)) {
+        vmask |= 1u << j;
+        lo = min(lo, kk[j]);
+        hi = max(hi, kk[j]);
+      }
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.wlo[wave] = lo;
+    sh.whi[wave] = hi;
+  }
+  __syncthreads();   // histograms cleared, per-wave extremes written
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    lo = min(lo, sh.wlo[w]);
+    hi = max(hi, sh.whi[w]);
+  }
+
+  uint32_t krem = (uint32_t)(k - has_cls);
+  uint32_t T = ~0u;
+  if (krem > 0) {
+    T = lo;
+    if (lo != hi) {
+      const int hb = 31 - __builtin_clz(lo ^ hi);          // highest bit where keys differ
+      uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);  // the common bits above it
+      uint32_t prefix = hi & pmask;
+      for (int top = hb, pass = 0; top >= 0; ++pass) {      // uniform; at most kPasses
+        const int width = min(kDigitBits, top + 1), shift = top - width + 1;
+        const int nb = 1 << width;
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        uint32_t* const fine = sh.fine[pass];
+        uint32_t* const coarse = sh.coarse[pass];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (((vmask >> j) & 1u) && (kk[j] & pmask) == prefix) {
+            const uint32_t d = (kk[j] >> shift) & dmask;
+            atomicAdd(&fine[d], 1u);
+            atomicAdd(&coarse[d >> 5], 1u);
+          }
+        __syncthreads();
+        // buckets high -> low on lanes 0, 1, ...: the bucket holding the krem-th largest
+        const int nbk = nb >= 32 ? nb >> 5 : 1, bpb = nb >= 32 ? 32 : nb;
+        const uint32_t cc = lane < nbk ? coarse[nbk - 1 - lane] : 0u;
+        const uint32_t ci = wave_inclusive_scan(cc);
+        const int cl = __ffsll((unsigned long long)__ballot(ci >= krem)) - 1;
+        const int cb = nbk - 1 - cl;
+        const uint32_t abk = (uint32_t)__builtin_amdgcn_readlane((int)(ci - cc), cl);
+        // its bins high -> low: the bin
+        const uint32_t fc = lane < bpb ? fine[cb * 32 + bpb - 1 - lane] : 0u;
+        const uint32_t fi = wave_inclusive_scan(fc);
+        const int fl = __ffsll((unsigned long long)__ballot(abk + fi >= krem)) - 1;
+        const uint32_t bin = (uint32_t)(cb * 32 + bpb - 1 - fl);
+        const uint32_t ab = abk + (uint32_t)__builtin_amdgcn_readlane((int)(fi - fc), fl);
+        const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)fc, fl);
+        prefix |= bin << shift;
+        pmask |= dmask << shift;
+        krem -= ab;
+        if (cnt == krem) {   // every key of the bin is kept
+          krem = (uint32_t)k;
+          break;
+        }
+        top = shift - 1;
+      }
+      T = prefix;
+    }
+  }
+
+  // kept = the class token, every key above T, the first krem copies of T in index order
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const bool v = (vmask >> j) & 1u;
+    gt += (has_cls && i0 + j == 0) || (v && kk[j] > T) ? 1u : 0u;
+    eq += v && kk[j] == T ? 1u : 0u;
+  }
+  // (counts <= L <= 16384 fit 16 bits each)
+  const uint32_t before = (uint32_t)block_exclusive_scan((int)(gt | (eq << 16)), sh.wsum);
+  uint32_t e = before >> 16;
+  uint32_t pos = (before & 0xFFFFu) + min(e, krem);
+  const bool copy = c0.src || c1.src;
   int32_t* kb = kept + (size_t)b * k;
-  for (int i = i0; i < i1; ++i) {
-    if (((keepbits >> (i - i0)) & 1u) && pos < k) {
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = i0 + j;
+    const bool v = (vmask >> j) & 1u;
+    bool keep = (has_cls && i == 0) || (v && kk[j] > T);
+    if (v && kk[j] == T) {
+      keep = e < krem;
+      ++e;
+    }
+    if (keep && pos < (uint32_t)k) {
       if (lead) {
         kb[pos] = i;
         if (ids_out) ids_out[(size_t)b * k + pos] = ids_in ? ids_in[rb + i] : i;
       }
-      keys[pos] = (uint32_t)i;  // kept list (every key read above is done: scan barrier)
+      if (copy) list[pos] = (uint32_t)i;
       ++pos;
     }
   }
-  if (!c0.src && !c1.src) return;
+  if (!copy) return;
   __syncthreads();
-  copy_rows(c0, keys, b, L, k, cj0, cj1);
-  copy_rows(c1, keys, b, L, k, cj0, cj1);
+  const int cj0 = (int)((long long)g * k / G), cj1 = (int)((long long)(g + 1) * k / G);
+  copy_rows(c0, list, b, L, k, cj0, cj1);
+  copy_rows(c1, list, b, L, k, cj0, cj1);
 }
 
 __global__ void iota_kernel(int32_t* ids, int L, long long total) {
@@ -683,13 +688,32 @@ hipError_t launch_pool(Dtype dt, const void* x, const void* gamma, const void* b
 
 hipError_t launch_score_rows(Dtype dt, const void* fx, const void* x, float* scores, int M, int C,
                              int dist, hipStream_t stream) {
-  const int grid = (M + 15) / 16;
-  if (dt == kBF16)
-    score_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(fx),
-                                                 static_cast<const bf16*>(x), scores, M, C, dist);
-  else
-    score_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(fx),
-                                                  static_cast<const float*>(x), scores, M, C, dist);
+  const bool narrow = (C >> 3) <= 64;   // rows of up to 64 chunks: 8 lanes per row
+  const int grid = narrow ? (M + 31) / 32 : (M + 15) / 16;
+  if (dt == kBF16) {
+    const bf16 *a = static_cast<const bf16*>(fx), *b = static_cast<const bf16*>(x);
+    if (narrow) score_kernel<bf16, 8><<<grid, 256, 0, stream>>>(a, b, scores, M, C, dist);
+    else score_kernel<bf16, 16><<<grid, 256, 0, stream>>>(a, b, scores, M, C, dist);
+  } else {
+    const float *a = static_cast<const float*>(fx), *b = static_cast<const float*>(x);
+    if (narrow) score_kernel<float, 8><<<grid, 256, 0, stream>>>(a, b, scores, M, C, dist);
+    else score_kernel<float, 16><<<grid, 256, 0, stream>>>(a, b, scores, M, C, dist);
+  }
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_topk_r(int grid, size_t lds, const float* scores, const float* part, int P,
+                         int dist, int L, int k, int has_cls, float* scores_out, int32_t* kept,
+                         const int32_t* ids_in, int32_t* ids_out, const RowCopy& c0,
+                         const RowCopy& c1, int G, hipStream_t stream) {
+  // the kept list takes up to RS_MAX_TOKENS words of dynamic LDS beside the static part
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&topk_kernel<R>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      RS_MAX_TOKENS * 4);
+  if (attr != hipSuccess) return attr;
+  topk_kernel<R><<<grid, kTopkThreads, lds, stream>>>(scores, part, P, dist, L, k, has_cls,
+                                                      scores_out, kept, ids_in, ids_out, c0, c1, G);
   return hipGetLastError();
 }
 
@@ -702,9 +726,17 @@ hipError_t launch_topk(const float* scores, const float* part, int P, int dist, 
     c[i] = {static_cast<const char*>(copies[i].src), static_cast<char*>(copies[i].dst),
             copies[i].row_bytes / 16};
   const int G = ncopies > 0 ? topk_copy_split(B) : 1;
-  topk_kernel<<<B * G, kTopkThreads, 0, stream>>>(scores, part, P, dist, L, k, has_cls, scores_out,
-                                                  kept, ids_in, ids_out, c[0], c[1], G);
-  return hipGetLastError();
+  const size_t lds = ncopies > 0 ? (size_t)k * 4 : 0;
+  const int grid = B * G;
+  if (L <= kTopkThreads)
+    return launch_topk_r<1>(grid, lds, scores, part, P, dist, L, k, has_cls, scores_out, kept, ids_in, ids_out, c[0], c[1], G, stream);
+  if (L <= 2 * kTopkThreads)
+    return launch_topk_r<2>(grid, lds, scores, part, P, dist, L, k, has_cls, scores_out, kept, ids_in, ids_out, c[0], c[1], G, stream);
+  if (L <= 4 * kTopkThreads)
+    return launch_topk_r<4>(grid, lds, scores, part, P, dist, L, k, has_cls, scores_out, kept, ids_in, ids_out, c[0], c[1], G, stream);
+  if (L <= 8 * kTopkThreads)
+    return launch_topk_r<8>(grid, lds, scores, part, P, dist, L, k, has_cls, scores_out, kept, ids_in, ids_out, c[0], c[1], G, stream);
+  return launch_topk_r<32>(grid, lds, scores, part, P, dist, L, k, has_cls, scores_out, kept, ids_in, ids_out, c[0], c[1], G, stream);
 }
 
 hipError_t launch_iota(int32_t* ids, int B, int L, hipStream_t stream) {
