@@ -194,6 +194,98 @@ def summarize(dirs, workload):
     return out
 
 
+def stage_shapes(wl):
+    """(L, k) of each prune stage of the workload, in order."""
+    import numpy as np
+    out, L = [], wl.L
+    for r in wl.keep_ratios:
+        k = int(np.floor(r * L + 0.5))
+        out.append((L, k))
+        L = k
+    return out
+
+
+def standalone_bytes(wl, L, k):
+    """Algorithmic bytes of one rs_score and one rs_topk_gather call at a stage (the same
+    figures as the standalone measurement)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    M = wl.B * L
+    return {"score": 2.0 * M * wl.C * e + 4.0 * M,
+            "topk": wl.B * (4.0 * L + 2.0 * k * wl.C * e + 4.0 * k)}
+
+
+def summarize_standalone(dirs, workload):
+    """Per-stage dispatch durations and (when the databases hold FETCH_SIZE / WRITE_SIZE)
+    copy-calibrated HBM bytes of the standalone rs_score / rs_topk_gather dispatches.  The
+    stages are told apart by launch shape (grid size, and the top-k's dynamic LDS of k
+    words) in order of first appearance; the copy probe is the top-k dispatch of over 100 us."""
+    import collections
+    import glob
+    import sqlite3
+    import synth
+    wl = synth.WORKLOADS[workload]
+    shapes = stage_shapes(wl)
+    groups = collections.OrderedDict()   # (class, grid, lds) -> {"dur": [], counter: []}
+    probe = collections.defaultdict(list)
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+            cur = sqlite3.connect(path).cursor()
+            names = dict(cur.execute("select id, kernel_name from kernel_symbols"))
+            disp = collections.OrderedDict()
+            for did, kid, dur, gx, gy, gz, lds in cur.execute(
+                    "select dispatch_id, kernel_id, duration, grid_x, grid_y, grid_z, lds_size "
+                    "from kernels order by start"):
+                kc = kernel_class(names.get(kid, ""))
+                if kc in ("score", "topk"):
+                    disp[did] = (kc, gx * gy * gz, lds, dur)
+            pmc = collections.defaultdict(dict)
+            try:
+                for did, cname, cval in cur.execute(
+                        "select dispatch_id, counter_name, sum(counter_value) from pmc_events "
+                        "group by dispatch_id, counter_name"):
+                    pmc[did][cname] = cval
+            except sqlite3.OperationalError:
+                pass
+            for did, (kc, grid, lds, dur) in disp.items():
+                if kc == "topk" and dur > 100e3:
+                    for c, v in pmc[did].items():
+                        probe[c].append(v)
+                    continue
+                g = groups.setdefault((kc, grid, lds), collections.defaultdict(list))
+                g["duration_ns"].append(dur)
+                for c, v in pmc[did].items():
+                    g[c].append(v)
+    known = 8 * 16384 * 8192 * 2
+    fac = {c: known / (sum(v) / len(v) * 1024.0) for c, v in probe.items() if v}
+    stages = {"score": [], "topk": []}
+    for (kc, grid, lds), g in groups.items():
+        stages[kc].append((grid, lds, g))
+    out = {"workload": workload, "copy_probe_scale": fac, "stages": []}
+    for i, (L, k) in enumerate(shapes):
+        algo = standalone_bytes(wl, L, k)
+        st = {"L": L, "k": k}
+        for kc in ("score", "topk"):
+            if i >= len(stages[kc]):
+                continue
+            grid, lds, g = stages[kc][i]
+            dur = sorted(g["duration_ns"])
+            row = {"dispatches": len(dur), "avg_us": round(sum(dur) / len(dur) / 1e3, 2),
+                   "median_us": round(dur[len(dur) // 2] / 1e3, 2), "grid": grid, "lds": lds,
+                   "algorithmic_bytes": int(algo[kc])}
+            row["frac_hbm_median"] = round(algo[kc] / (dur[len(dur) // 2] * 1e-9) / (PEAK["hbm"] * 1e9), 4)
+            t = 0.0
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                if g.get(c) and c in fac:
+                    row[c + "_bytes"] = int(sum(g[c]) / len(g[c]) * 1024.0 * fac[c])
+                    t += row[c + "_bytes"]
+            if "FETCH_SIZE_bytes" in row and "WRITE_SIZE_bytes" in row:
+                row["traffic_bytes"] = int(t)
+                row["traffic_over_algorithmic"] = round(t / algo[kc], 3)
+            st[kc] = row
+        out["stages"].append(st)
+    return out
+
+
 def kernel_sources_sha256():
     import hashlib
     src = os.path.join(ROOT, "vit_token_pruning_amd", "csrc")
@@ -224,7 +316,9 @@ def standalone(wl, steps):
     bytes / kernel time against 8 TB/s.  Inputs rotate over >= 512 MiB of buffers (twice the
     256 MB Infinity Cache) so every call reads from HBM.  Bytes per call: rs_score reads
     f and x (2 M C e) and writes 4 M; rs_topk_gather reads 4 L scores and the k kept rows
-    (k C e) per sample and writes k C e + 4 k."""
+    (k C e) per sample and writes k C e + 4 k.  `us` is the time per call of `steps` calls
+    captured in one HIP graph (replayed; no host launch cost between calls), `us_eager` the
+    same calls launched one by one from Python (bounded below by the host's launch rate)."""
     import numpy as np
     import torch
     from vit_token_pruning_amd import _native as N
@@ -232,7 +326,6 @@ def standalone(wl, steps):
     e = 2 if wl.dtype == "bf16" else 4
     lib = N.lib()
     code = N.RS_BF16 if wl.dtype == "bf16" else N.RS_F32
-    stream = torch.cuda.current_stream()
     out = []
     L = wl.L
     for pl, r in zip(wl.prune_layers, wl.keep_ratios):
@@ -246,18 +339,19 @@ def standalone(wl, steps):
         sc = [torch.empty(B, L, device="cuda", dtype=torch.float32) for _ in range(nbuf)]
         kept = torch.empty(B, k, device="cuda", dtype=torch.int32)
         xk = torch.empty(B, k, C, device="cuda", dtype=dt)
-        hs = stream.cuda_stream
 
-        def score(i):
+        def score(i, hs):
             N.check("rs_score", lib.rs_score(fx[i].data_ptr(), xs[i].data_ptr(), B, L, C, code,
                                              sc[i].data_ptr(), hs))
 
-        def select(i):
+        def select(i, hs):
             N.check("rs_topk_gather", lib.rs_topk_gather(sc[i].data_ptr(), xs[i].data_ptr(), B, L, C,
                                                          code, k, wl.has_cls, kept.data_ptr(),
                                                          xk.data_ptr(), hs))
+        stream = torch.cuda.current_stream()
         for i in range(nbuf):
-            score(i)
+            score(i, stream.cuda_stream)
+            select(i, stream.cuda_stream)
         torch.cuda.synchronize()
         res = {"after_block": pl, "L": L, "k": k, "M": M, "buffers_MiB": round(nbuf * 2 * M * C * e / 2**20)}
         for name, fn, nbytes in (("score", score, 2.0 * M * C * e + 4.0 * M),
@@ -265,17 +359,78 @@ def standalone(wl, steps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for it in range(steps):
-                fn(it % nbuf)
+                fn(it % nbuf, stream.cuda_stream)
             e1.record(stream)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / steps
+            us_eager = e0.elapsed_time(e1) * 1e3 / steps
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                hs = torch.cuda.current_stream().cuda_stream
+                for it in range(steps):
+                    fn(it % nbuf, hs)
+            graph.replay()
+            torch.cuda.synchronize()
+            reps = 5
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
             gbs = nbytes / (us * 1e-6) / 1e9
-            res[name] = {"us": round(us, 2), "bytes": int(nbytes), "GB_s": round(gbs, 1),
-                         "frac_hbm": round(gbs / PEAK["hbm"], 4)}
+            res[name] = {"us": round(us, 2), "us_eager": round(us_eager, 2), "bytes": int(nbytes),
+                         "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK["hbm"], 4)}
+            del graph
+        # the last replayed call's selection equals an eager call on the same input
+        last = (steps - 1) % nbuf
+        kg, xg = kept.clone(), xk.clone()
+        select(last, stream.cuda_stream)
+        torch.cuda.synchronize()
+        res["graph_replay_matches_eager"] = bool(torch.equal(kg, kept) and torch.equal(xg, xk))
         out.append(res)
         del fx, xs, sc
         torch.cuda.empty_cache()
         L = k
+    return out
+
+
+PROBE_MODES = {0: "exp2", 1: "fma", 2: "softmax_tile", 3: "mfma_tile", 4: "softmax_and_mfma_tile"}
+
+
+def probe_ceiling(torch, workgroups=1024, iters=4000):
+    """The attention kernel's vector-unit ceiling, measured (rs_probe_throughput): issue
+    cycles per SIMD for one hardware exp2 and one FMA (wave64 instructions), and for one
+    64-key x 16-query tile of the fused attention (per wave: 16 MFMA 16x16x32 for S = K Q^T
+    and O += V^T P^T, and the softmax of the lane's 16 scores), its softmax alone, its
+    matrix work alone and both in one wave.  Cycles are SIMD-cycles at 2.4 GHz over the
+    1024 SIMDs; 1024 workgroups of four waves (four waves per SIMD) fill the chip.  The
+    tile's flop / (cycles with both) is the most the attention kernel can reach while its
+    softmax issues as the probe does."""
+    from vit_token_pruning_amd import _native as N
+    lib = N.lib()
+    sink = torch.empty(workgroups * 256, device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    waves = workgroups * 4
+    out = {"workgroups": workgroups, "waves_per_simd": 4, "iters": iters, "clock_ghz": 2.4}
+    for mode, name in PROBE_MODES.items():
+        def go():
+            N.check("rs_probe_throughput", lib.rs_probe_throughput(mode, workgroups, iters,
+                                                                   sink.data_ptr(), stream.cuda_stream))
+        go()
+        torch.cuda.synchronize()
+        ms = time_steps(go, 3, torch)
+        simd_cycles = ms * 1e-3 * 2.4e9 * 1024
+        per = simd_cycles / (waves * iters)
+        if mode in (0, 1):
+            out[name + "_cycles_per_instruction"] = round(per / 16, 3)
+        else:
+            out[name + "_cycles"] = round(per, 1)
+        out[name + "_ms"] = round(ms, 4)
+    tile_flop = 2 * 2 * 16 * 64 * 64
+    both = out["softmax_and_mfma_tile_cycles"]
+    out["mfma_cycles_per_instruction"] = round(out["mfma_tile_cycles"] / 16, 3)
+    out["attention_ceiling_tflops"] = round(tile_flop / both * 1024 * 2.4e9 / 1e12, 1)
+    out["attention_ceiling_frac_of_peak"] = round(16 * 16 / both, 4)   # 16 MFMA x 16 cycles at peak
     return out
 
 
@@ -500,11 +655,19 @@ def main():
                     help="skip the standalone rs_score / rs_topk_gather measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 2 GiB copy through the gather kernel (counter calibration)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only measure the attention vector-unit ceiling (throughput probe) and exit")
+    ap.add_argument("--summarize-standalone", nargs="+", metavar="DIR",
+                    help="per-stage durations / HBM bytes of rs_score and rs_topk_gather from "
+                         "rocprofv3 result directories of a --standalone run, and exit")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 --pmc result directories and exit (no GPU use)")
     args = ap.parse_args()
     if args.summarize:
         print(json.dumps(summarize(args.summarize, args.workload), indent=1))
+        return
+    if args.summarize_standalone:
+        print(json.dumps(summarize_standalone(args.summarize_standalone, args.workload), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -520,9 +683,16 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.depth == 1:
         sys.exit("pick an encoder workload (the single block is reported under `configs`)")
+    if args.probe:
+        torch.cuda.set_device(0)
+        print(json.dumps({"metric": "attention vector-unit ceiling (rs_probe_throughput)",
+                          **probe_ceiling(torch)}), flush=True)
+        return
     if args.standalone:
         torch.cuda.set_device(0)
         res = standalone(wl, args.steps)
+        if args.copy_probe:
+            copy_probe(rs, torch)
         print(json.dumps({"metric": "standalone rs_score / rs_topk_gather HBM throughput",
                           "workload": wl.name, "unit": "GB/s", "peak": PEAK["hbm"], "stages": res}),
               flush=True)
@@ -616,12 +786,23 @@ def main():
                                  "note": "RTX A6000, whole forward pass; not the same work",
                                  "ratio": round(value / v, 2)}
     context = not args.no_breakdown
+    if context and "attention" in per:
+        ceil = probe_ceiling(torch)
+        att = per["attention"]
+        att_tf = att["work"] / (att["ms"] / 1e3) / 1e12
+        bound_tf = min(PEAK["mfma"], ceil["attention_ceiling_tflops"])
+        line["attention"] = {"achieved_tflops_single_lane": round(att_tf, 2), "mfma_peak": PEAK["mfma"],
+                             "valu_ceiling_tflops": ceil["attention_ceiling_tflops"],
+                             "bound_tflops": bound_tf, "frac_of_bound": round(att_tf / bound_tf, 4),
+                             "probe": ceil}
+        log("attention:", line["attention"]["achieved_tflops_single_lane"], "TFLOP/s of a",
+            bound_tf, "TFLOP/s bound")
     if context and not args.no_hbm:
         res = standalone(wl, 50)
         line["hbm_kernels"] = {
             "unit": "GB/s", "peak": PEAK["hbm"],
             "note": "rs_score and rs_topk_gather alone at each prune stage's shape; algorithmic "
-                    "bytes / event time, inputs rotating over >= 512 MiB",
+                    "bytes / time per call (50 calls in one HIP graph), inputs rotating over >= 512 MiB",
             "stages": res}
         log("standalone HBM kernels:", [(r["L"], r["score"]["frac_hbm"], r["topk_gather"]["frac_hbm"])
                                          for r in res])

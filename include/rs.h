@@ -332,6 +332,21 @@ typedef enum {
 rs_status rs_timing_begin(int kernel_id);
 rs_status rs_timing_end(float* total_ms, int* launches, double* work);
 
+/* ---- throughput probe (measurement support; not part of the method) ---------------
+ * Runs `workgroups` workgroups of 256 threads of a probe kernel on `stream`; each wave
+ * iterates `iters` times over the body of `mode` on register data:
+ *   0  16 independent hardware exp2          1  16 independent fp32 FMAs
+ *   2  the fused attention's softmax of one 64-key x 16-query tile (each lane's 16
+ *      scores: maximum, rescale test, exp2, running sum, bf16 packing of P)
+ *   3  16 MFMA 16x16x32 bf16 (the matrix work of that tile)
+ *   4  the bodies of 2 and 3 interleaved in one wave on independent registers
+ * Their rates bound the attention kernel: per tile, the matrix cores need the mode-3 time
+ * and the vector units the mode-2 time, and mode 4 shows how far one wave overlaps them.
+ * sink: device, workgroups * 256 floats, caller-owned; receives one value per thread so
+ * the work is kept.  Asynchronous.  RS_ERR_INVALID_ARG for a mode outside 0..4,
+ * workgroups < 1, iters < 1 or a null sink. */
+rs_status rs_probe_throughput(int mode, int workgroups, int iters, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

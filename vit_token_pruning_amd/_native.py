@@ -103,6 +103,7 @@ def lib():
         "rs_last_error": (ctypes.c_char_p, []),
         "rs_set_max_lanes": (c_int, [c_int]),
         "rs_get_max_lanes": (c_int, []),
+        "rs_probe_throughput": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p]),
         "rs_timing_begin": (c_int, [c_int]),
         "rs_timing_end": (c_int, [ctypes.POINTER(c_float), P_INT, P_DBL]),
     }

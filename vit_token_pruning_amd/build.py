@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librs.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["rs_gemm.hip", "rs_attn.hip", "rs_attn_map.hip", "rs_rowops.hip", "rs_noalloc.hip"]
+DEVICE_SOURCES = ["rs_gemm.hip", "rs_attn.hip", "rs_attn_map.hip", "rs_rowops.hip", "rs_noalloc.hip", "rs_probe.hip"]
 HOST_SOURCES = ["rs_api.cpp"]
 
 HIP_FLAGS = [
@@ -34,6 +34,7 @@ HIP_FLAGS = [
 # accumulator-register results cost a copy each way (112 moves per tile).  The GEMMs keep
 # the default (measured slower with it).
 SOURCE_FLAGS = {"rs_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "rs_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "rs_attn_map.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = [
     "-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",

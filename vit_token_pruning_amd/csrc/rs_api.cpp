@@ -1075,6 +1075,16 @@ rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
   return run_head(*desc, *head, vw.enc_out, B, L_final, features, logits, vw.head, nullptr, stream);
 }
 
+rs_status rs_probe_throughput(int mode, int workgroups, int iters, float* sink,
+                              hipStream_t stream) {
+  if (mode < 0 || mode > 4) return fail(RS_ERR_INVALID_ARG, "probe mode must be 0 .. 4");
+  if (workgroups < 1 || iters < 1) return fail(RS_ERR_INVALID_ARG, "workgroups and iters must be >= 1");
+  rs_status s;
+  if ((s = check_ptr(sink, "sink")) != RS_OK) return s;
+  RS_HIP(rs::launch_probe(mode, workgroups, iters, sink, stream));
+  return RS_OK;
+}
+
 rs_status rs_set_max_lanes(int lanes) {
   if (lanes < 1 || lanes > kMaxLanes) return fail(RS_ERR_INVALID_ARG, "lanes must be 1 .. 4");
   g_max_lanes.store(lanes);

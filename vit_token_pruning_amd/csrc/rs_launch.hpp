@@ -193,6 +193,9 @@ inline int topk_copy_split(int B) {
   return g < 1 ? 1 : (g > kTopkMaxSplit ? kTopkMaxSplit : g);
 }
 
+// Throughput probe (rs_probe.hip): `workgroups` x 256 threads, body `mode`, `iters` times.
+hipError_t launch_probe(int mode, int workgroups, int iters, float* sink, hipStream_t stream);
+
 // ids[b][i] = i
 hipError_t launch_iota(int32_t* ids, int B, int L, hipStream_t stream);
 

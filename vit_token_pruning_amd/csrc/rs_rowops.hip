@@ -378,15 +378,21 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(v, 0u, MaxU32()), 63);
 }
-// exclusive prefix sum over the threads of the workgroup (kTopkWaves waves)
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
+// Workgroup barrier that waits only for this wave's LDS operations: the top-k's barriers
+// order LDS traffic alone, and __syncthreads() would also wait for the global stores of
+// scores, indices and ids still in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// exclusive prefix sum over the threads of the workgroup (kTopkWaves waves); wsum is
+// written once, so a workgroup calls this once
+__device__ __forceinline__ int block_exclusive_scan_once(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = (int)wave_inclusive_scan((uint32_t)v);
   if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkWaves - 1; ++w) before += w < wave ? wsum[w] : 0;
   return before + incl - v;
 }
 
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     sh.wlo[wave] = lo;
     sh.whi[wave] = hi;
   }
-  __syncthreads();   // histograms cleared, per-wave extremes written
+  lds_barrier();   // histograms cleared, per-wave extremes written
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
     lo = min(lo, sh.wlo[w]);
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             atomicAdd(&fine[d], 1u);
             atomicAdd(&coarse[d >> 5], 1u);
           }
-        __syncthreads();
+        lds_barrier();
         // buckets high -> low on lanes 0, 1, ...: the bucket holding the krem-th largest
         const int nbk = nb >= 32 ? nb >> 5 : 1, bpb = nb >= 32 ? 32 : nb;
         const uint32_t cc = lane < nbk ? coarse[nbk - 1 - lane] : 0u;
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     eq += v && kk[j] == T ? 1u : 0u;
   }
   // (counts <= L <= 16384 fit 16 bits each)
-  const uint32_t before = (uint32_t)block_exclusive_scan((int)(gt | (eq << 16)), sh.wsum);
+  const uint32_t before = (uint32_t)block_exclusive_scan_once((int)(gt | (eq << 16)), sh.wsum);
   uint32_t e = before >> 16;
   uint32_t pos = (before & 0xFFFFu) + min(e, krem);
   const bool copy = c0.src || c1.src;
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
   }
   if (!copy) return;
-  __syncthreads();
+  lds_barrier();
   const int cj0 = (int)((long long)g * k / G), cj1 = (int)((long long)(g + 1) * k / G);
   copy_rows(c0, list, b, L, k, cj0, cj1);
   copy_rows(c1, list, b, L, k, cj0, cj1);
