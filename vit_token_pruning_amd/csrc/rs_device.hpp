@@ -29,6 +29,15 @@ __device__ __forceinline__ void load_frag(Frag8<float>& f, const void* p) {
   f.v[0] = ((const u32x4*)p)[0];
   f.v[1] = ((const u32x4*)p)[1];
 }
+// Streaming reads (data read once and not again by this kernel): non-temporal loads, which
+// do not displace reused lines from the caches.
+__device__ __forceinline__ void load_frag_nt(Frag8<bf16>& f, const void* p) {
+  f.v = __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void load_frag_nt(Frag8<float>& f, const void* p) {
+  f.v[0] = __builtin_nontemporal_load((const u32x4*)p);
+  f.v[1] = __builtin_nontemporal_load((const u32x4*)p + 1);
+}
 __device__ __forceinline__ void store_frag(void* p, const Frag8<bf16>& f) { *(u32x4*)p = f.v; }
 __device__ __forceinline__ void store_frag(void* p, const Frag8<float>& f) {
   ((u32x4*)p)[0] = f.v[0];
