@@ -194,6 +194,54 @@ def summarize(dirs, workload):
     return out
 
 
+def trace_class(mangled: str):
+    """Kernel class of a dispatch for the per-kernel time table: the library's timing class,
+    with the split-K partial / reduction kernels and the two LayerNorm preparation kernels
+    told apart."""
+    kc = kernel_class(mangled)
+    if kc is None:
+        return None
+    if "splitk_reduce_kernel" in mangled:
+        return kc + " (split-K reduction)"
+    if "gemm_kernel" in mangled and "ELb1EE" in mangled:
+        return kc + " (split-K partial)"
+    if kc == "ln_prep":
+        return "ln_prep (fold)" if "fold_kernel" in mangled else "ln_prep (row stats)"
+    return kc
+
+
+def summarize_trace(dirs):
+    """Markdown table of per-dispatch durations by kernel class from rocprofv3
+    --kernel-trace -f csv output (library kernels only)."""
+    import collections
+    import csv
+    import glob
+    durs = collections.defaultdict(list)
+    names = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = r["Kernel_Name"]
+                    kc = trace_class(name)
+                    if kc is None:
+                        continue
+                    durs[kc].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                    names.setdefault(kc, name)
+    total = sum(sum(v) for v in durs.values())
+    lines = ["| kernel (class) | dispatches | total ms | avg us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    for kc, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {kc} | {len(v)} | {sum(v) / 1e6:.3f} | {sum(v) / len(v) / 1e3:.2f} | "
+                     f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} | {100.0 * sum(v) / total:.2f} |")
+    lines.append("")
+    lines.append("Symbols:")
+    lines.append("")
+    for kc in sorted(names):
+        lines.append(f"- {kc}: `{names[kc].split('(')[0] if not names[kc].startswith('_Z') else names[kc]}`")
+    return "\n".join(lines)
+
+
 def stage_shapes(wl):
     """(L, k) of each prune stage of the workload, in order."""
     import numpy as np
@@ -657,6 +705,9 @@ def main():
                     help="also run a 2 GiB copy through the gather kernel (counter calibration)")
     ap.add_argument("--probe", action="store_true",
                     help="only measure the attention vector-unit ceiling (throughput probe) and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DIR",
+                    help="markdown table of kernel durations by class from rocprofv3 --kernel-trace "
+                         "-f csv directories, and exit")
     ap.add_argument("--summarize-standalone", nargs="+", metavar="DIR",
                     help="per-stage durations / HBM bytes of rs_score and rs_topk_gather from "
                          "rocprofv3 result directories of a --standalone run, and exit")
@@ -665,6 +716,9 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         print(json.dumps(summarize(args.summarize, args.workload), indent=1))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
         return
     if args.summarize_standalone:
         print(json.dumps(summarize_standalone(args.summarize_standalone, args.workload), indent=1))
