@@ -276,3 +276,15 @@ def test_attention_noalloc_validation(N):
     assert lib.rs_attention_noalloc(ctypes.byref(d), None, 2, 197, FAKE, None, None, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_attention_noalloc(ctypes.byref(d), FAKE, 2, 197, FAKE + 4, None, None, None, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_attention_noalloc(ctypes.byref(d), FAKE, 0, 197, FAKE, None, None, None, None) == N.RS_ERR_INVALID_ARG
+
+
+def test_probe_validation(N):
+    """rs_probe_throughput rejects, before any HIP call, a mode outside 0..4, an empty grid or
+    iteration count, and a null sink."""
+    lib = N.lib()
+    assert lib.rs_probe_throughput(5, 1024, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert b"mode" in lib.rs_last_error()
+    assert lib.rs_probe_throughput(-1, 1024, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_probe_throughput(0, 0, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_probe_throughput(0, 1024, 0, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_probe_throughput(2, 1024, 10, None, None) == N.RS_ERR_INVALID_ARG

@@ -72,3 +72,90 @@ def test_busy_fraction_overall_and_per_launch_shape(tmp_path):
     assert abs(g[str(256 * 612)]["mfma_busy_frac"] - 0.125) < 1e-12
     # overall: mean counter over mean duration
     assert abs(k["mfma_busy_frac"] - 6.144e6 / (1024 * (40000 / 3) * 2.4)) < 1e-12
+
+
+SCORE = "_ZN2rs12_GLOBAL__N_112score_kernelIDF16bEEvPKT_S4_Pfiii"
+TOPK1 = "rs::(anonymous namespace)::topk_kernel<1>(float const*, float const*, int, int, int, int, int, float*, int*, int const*, int*, rs::(anonymous namespace)::RowCopy, rs::(anonymous namespace)::RowCopy, int)"
+
+
+def _sa_db(path, dispatches, counters):
+    """dispatches: (id, kernel_id, duration_ns, grid_x, lds, start); kernel 1 = rs_score's,
+    2 = the top-k's; counters: (dispatch_id, name, value)."""
+    con = sqlite3.connect(path)
+    con.execute("create table kernel_symbols (id integer, kernel_name text)")
+    con.executemany("insert into kernel_symbols values (?, ?)", [(1, SCORE), (2, TOPK1)])
+    con.execute("create table kernels (dispatch_id integer, kernel_id integer, duration integer, "
+                "grid_x integer, grid_y integer, grid_z integer, lds_size integer, start integer)")
+    con.executemany("insert into kernels values (?, ?, ?, ?, 1, 1, ?, ?)", dispatches)
+    con.execute("create table pmc_events (dispatch_id integer, counter_name text, counter_value real)")
+    con.executemany("insert into pmc_events values (?, ?, ?)", counters)
+    con.commit()
+    con.close()
+
+
+def test_standalone_summary_per_stage(tmp_path):
+    """bench.py --summarize-standalone: stages told apart by launch shape in order of first
+    appearance, median durations against the algorithmic bytes of each stage, and traffic
+    calibrated by the copy probe (the top-k dispatch of over 100 us)."""
+    known = 8 * 16384 * 8192 * 2
+    d = tmp_path / "sa"
+    d.mkdir()
+    # DeiT-S stages: L 197 -> 138 -> 97 -> 68 (batch 256, C 384, bf16)
+    disp, ctr, t = [], [], 0
+    did = 0
+    for stage, (grid, lds) in enumerate(((256 * 3152, 138 * 4), (256 * 2208, 97 * 4), (256 * 1552, 68 * 4))):
+        for rep, dur in enumerate((10000, 12000, 14000)):     # score: median 12 us
+            did += 1; t += 1
+            disp.append((did, 1, dur + 1000 * stage, grid, 0, t))
+            ctr += [(did, "FETCH_SIZE", 1000.0 * (stage + 1)), (did, "WRITE_SIZE", 10.0)]
+        for rep, dur in enumerate((8000, 9000, 30000)):       # top-k: median 9 us
+            did += 1; t += 1
+            disp.append((did, 2, dur, 512 * 512, lds, t))
+            ctr += [(did, "FETCH_SIZE", 500.0), (did, "WRITE_SIZE", 400.0)]
+    did += 1; t += 1
+    disp.append((did, 2, 700000, 512 * 512, 16384 * 4, t))        # the copy probe
+    ctr += [(did, "FETCH_SIZE", known / 1024 / 2), (did, "WRITE_SIZE", known / 1024)]
+    _sa_db(d / "a.db", disp, ctr)
+    out = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--summarize-standalone", str(d),
+                          "--workload", "deit_s"], capture_output=True, text=True, check=True, cwd=ROOT).stdout
+    s = json.loads(out)
+    assert abs(s["copy_probe_scale"]["FETCH_SIZE"] - 2.0) < 1e-12
+    assert [(st["L"], st["k"]) for st in s["stages"]] == [(197, 138), (138, 97), (97, 68)]
+    st0 = s["stages"][0]
+    assert st0["score"]["dispatches"] == 3 and st0["score"]["median_us"] == 12.0
+    assert st0["topk"]["dispatches"] == 3 and st0["topk"]["median_us"] == 9.0   # probe excluded
+    algo_score = 2.0 * 256 * 197 * 384 * 2 + 4.0 * 256 * 197
+    algo_topk = 256 * (4.0 * 197 + 2.0 * 138 * 384 * 2 + 4.0 * 138)
+    assert st0["score"]["algorithmic_bytes"] == int(algo_score)
+    assert st0["topk"]["algorithmic_bytes"] == int(algo_topk)
+    assert abs(st0["score"]["frac_hbm_median"] - round(algo_score / 12e-6 / 8e12, 4)) < 1e-9
+    assert st0["score"]["FETCH_SIZE_bytes"] == int(1000.0 * 1024 * 2)
+    assert s["stages"][2]["score"]["FETCH_SIZE_bytes"] == int(3000.0 * 1024 * 2)
+    t0 = st0["topk"]
+    assert abs(t0["traffic_over_algorithmic"] - round((500.0 * 2 + 400.0) * 1024 / algo_topk, 3)) < 1e-9
+
+
+def test_trace_table(tmp_path):
+    """bench.py --summarize-trace: per-class totals of a kernel trace, split-K partial and
+    reduction dispatches and the two LayerNorm preparation kernels listed apart."""
+    d = tmp_path / "tr"
+    d.mkdir()
+    fc2 = FC1.replace("Li2ENS0_4Tile", "Li3ENS0_4Tile")
+    fc2_split = fc2.replace("ELb0EEEvPKT_", "ELb1EEEvPKT_")
+    rows = [(FC1, 0, 30000), (FC1, 100000, 150000), (fc2, 0, 60000), (fc2_split, 0, 20000),
+            ("_ZN2rs12_GLOBAL__N_111fold_kernelIDF16bEEvNS0_8FoldArgsE", 0, 7000),
+            ("_ZN2rs12_GLOBAL__N_116row_stats_kernelIDF16bEEvPKT_Pfii", 0, 9000),
+            ("void at::native::elementwise_kernel<...>", 0, 999999)]
+    with open(d / "x_kernel_trace.csv", "w") as f:
+        f.write('"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for name, a, b in rows:
+            f.write(f'"KERNEL_DISPATCH","{name}",{a},{b}\n')
+    out = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--summarize-trace", str(d)],
+                         capture_output=True, text=True, check=True, cwd=ROOT).stdout
+    lines = {l.split("|")[1].strip(): [c.strip() for c in l.split("|")[2:-1]]
+             for l in out.splitlines() if l.startswith("| ") and not l.startswith("| kernel")}
+    assert set(lines) == {"fc1", "fc2_score", "fc2_score (split-K partial)", "ln_prep (fold)",
+                          "ln_prep (row stats)"}
+    assert lines["fc1"][:3] == ["2", "0.080", "40.00"]           # 30 + 50 us
+    total = 30000 + 50000 + 60000 + 20000 + 7000 + 9000
+    assert abs(float(lines["fc2_score"][-1]) - 100.0 * 60000 / total) < 0.01
