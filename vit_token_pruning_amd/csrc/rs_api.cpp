@@ -324,7 +324,7 @@ std::vector<LaneStreams> g_lanes;
 rs::Dtype dtype_of(const rs_model_desc& d) { return d.dtype == RS_BF16 ? rs::kBF16 : rs::kF32; }
 
 // LayerNorm folding of blocks [b0, b0 + n): W_qkv diag(gamma1) with its c, d, and c, d of
-// fc1 against gamma2/beta2; up to four blocks (eight weights) per launch.
+// fc1 against gamma2/beta2; up to kMaxFoldJobs / 2 blocks per launch.
 rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const EncWs& ws, int b0,
                    int n, hipStream_t st) {
   for (int b = b0; b < b0 + n; b += rs::kMaxFoldJobs / 2) {

@@ -138,7 +138,7 @@ struct FoldJob {
   float* d;
   int rows;
 };
-constexpr int kMaxFoldJobs = 8;
+constexpr int kMaxFoldJobs = 32;   // 16 blocks per launch; the arguments stay under 4 KiB
 hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStream_t stream);
 
 // Fused attention, one (sample, head, 64-query block) per workgroup.

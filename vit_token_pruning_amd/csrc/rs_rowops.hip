@@ -63,6 +63,7 @@ struct FoldArgs {
   int njobs;
   int C;
 };
+static_assert(sizeof(FoldArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // 16 lanes per output row n of one job (four rows per wave): W'[n][k] = W[n][k] * gamma[k]
 // (rounded to the storage type; only if the job has an output), c[n] = sum_k W'[n][k] (or
