@@ -336,6 +336,8 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 constexpr int kTopkThreads = 512, kTopkWaves = kTopkThreads / 64;
+// score partials per token: 2 per 128-column tile of a row of at most RS_MAX_WIDTH columns
+constexpr int kMaxPartPairs = (RS_MAX_WIDTH + 127) / 128;
 // Radix select: 11-bit digits (at most three passes over a 32-bit key), each pass with its
 // own histogram of 2048 bins plus 64 buckets of 32 bins (the bucket counts let a wave find
 // the selected bin with two 64-lane scans instead of reading all 2048 bins).
@@ -482,15 +484,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     sv[j] = 0.f;
     if (i < L) {
       if (part) {
-        // the token's slice partials: quantity q of slice p at q * P + p
-        const float* pp = part + (rb + i) * (size_t)(dist == 2 ? 3 * P : P);
+        // the token's slice partials: quantity q of slice p at q * P + p (P even, <= 16,
+        // so 8-byte aligned pairs); every pair is requested before any is summed, and the
+        // sums run in slice order
+        const float2* pp = reinterpret_cast<const float2*>(part + (rb + i) * (size_t)(dist == 2 ? 3 * P : P));
+        const int P2 = P >> 1;
+        float2 v[kMaxPartPairs];
+#pragma unroll
+        for (int h = 0; h < kMaxPartPairs; ++h) v[h] = h < P2 ? pp[h] : make_float2(0.f, 0.f);
         float a = 0.f, aa = 0.f, bb = 0.f;
-        for (int q = 0; q < P; ++q) a += pp[q];
-        if (dist == 2)
-          for (int q = 0; q < P; ++q) {
-            aa += pp[P + q];
-            bb += pp[2 * P + q];
+#pragma unroll
+        for (int h = 0; h < kMaxPartPairs; ++h)
+          if (h < P2) {
+            a += v[h].x;
+            a += v[h].y;
           }
+        if (dist == 2) {
+#pragma unroll
+          for (int h = 0; h < kMaxPartPairs; ++h) v[h] = h < P2 ? pp[P2 + h] : make_float2(0.f, 0.f);
+          float2 w[kMaxPartPairs];
+#pragma unroll
+          for (int h = 0; h < kMaxPartPairs; ++h) w[h] = h < P2 ? pp[2 * P2 + h] : make_float2(0.f, 0.f);
+#pragma unroll
+          for (int h = 0; h < kMaxPartPairs; ++h)
+            if (h < P2) {
+              aa += v[h].x;
+              aa += v[h].y;
+              bb += w[h].x;
+              bb += w[h].y;
+            }
+        }
         sv[j] = finish_dist(dist, a, aa, bb);
       } else {
         sv[j] = scores[rb + i];
