@@ -664,11 +664,28 @@ def block_config(steps, rs, torch):
     ws = torch.empty(rs.workspace_bytes(spec, 1, wl.B, wl.L), dtype=torch.uint8, device="cuda")
     for _ in range(10):
         rs.block_forward(spec, w, x, k, workspace=ws)
-    ms = time_steps(lambda: rs.block_forward(spec, w, x, k, workspace=ws), steps, torch)
+    ms_eager = time_steps(lambda: rs.block_forward(spec, w, x, k, workspace=ws), steps, torch)
+    # the same steps captured in one HIP graph and replayed: at this size every kernel is a
+    # few microseconds, so one-by-one launches from the host set the eager rate
+    eager = rs.block_forward(spec, w, x, k, workspace=ws)
+    torch.cuda.synchronize()
+    per = 20
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per):
+            out = rs.block_forward(spec, w, x, k, workspace=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(out[key], eager[key]) for key in ("y", "scores", "kept_idx", "y_kept"))
+    reps = max(1, steps // per)
+    ms = time_steps(graph.replay, reps, torch) / per
     flop = 2.0 * wl.B * (12 * wl.L * wl.C ** 2 + 2 * wl.L ** 2 * wl.C)
     ach = flop / (ms / 1e3) / 1e12
+    del graph
     return {"value": round(wl.B / (ms / 1e3), 2), "unit": "sample-blocks/s",
-            "blocks_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 5), "steps": steps,
+            "blocks_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 5), "steps": reps * per,
+            "launch": "HIP graph of 20 steps, replayed", "graph_replay_matches_eager": same,
+            "eager": {"value": round(wl.B / (ms_eager / 1e3), 2), "ms_per_step": round(ms_eager, 5)},
             "dtype": "f32", "batch": wl.B, "tokens": wl.L, "keep_k": k, "C": wl.C,
             "tokens_per_s": round(wl.B * wl.L / (ms / 1e3), 1),
             "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK["mfma_f32"],
