@@ -111,13 +111,14 @@ def test_score_matches_oracle(dt, B, L, C):
     assert rs.score(torch.zeros(2, 3, 64, device="cuda"), torch.zeros(2, 3, 64, device="cuda")).abs().max() == 0
 
 
-# Boundaries of the one-wave selection (4 / 8 / 16 / 32 keys per lane up to 2048 tokens,
-# the workgroup path beyond) and score sets that stress the radix passes: every competing
-# score equal (no bit to resolve), two distinct values, scores spread over the whole float
-# range (keys differing in the top bit), and many NaNs.
+# Boundaries of the keys-per-thread instantiations of the selection (1, 2, 4, 8 and 32 keys
+# per thread: L up to 512, 1024, 2048, 4096 and 16384) and score sets that stress the radix
+# passes: every competing score equal (no bit to resolve), two distinct values, scores spread
+# over the whole float range (keys differing in the top bit), and many NaNs.
 BOUNDS = [(3, 256, 100, True), (3, 257, 100, False), (2, 512, 511, True), (2, 513, 2, False),
           (2, 1024, 1023, False), (2, 1025, 700, True), (2, 2048, 1024, False),
-          (2, 2049, 1024, True), (4, 1568, 1, True), (4, 1568, 1568, False)]
+          (2, 2049, 1024, True), (4, 1568, 1, True), (4, 1568, 1568, False),
+          (2, 4096, 2048, False), (2, 4097, 4000, True), (1, 8193, 1, False), (1, 12000, 11999, True)]
 
 
 @pytest.mark.parametrize("B,L,k,cls", BOUNDS)
