@@ -9,7 +9,8 @@ from oracle import rs_oracle as O
 # Agreement rules (per block):
 SCORE_REL = 1e-2          # |s_gpu - s_ora| <= 1e-2 * s_ora for every token
 BAND_REL = 1e-2           # tie band around the k-th score for the kept-set rule
-BF16_OUT_ABS = 2e-2       # max |x_hat_gpu - x_hat_ora| <= 2e-2 * RMS(block input), bf16
+BF16_OUT_ABS = 2e-2       # max |x_hat_gpu - x_hat_ora| <= 2e-2 * RMS(block input), bf16,
+                          # plus half a bf16 ulp of the stored value (its own rounding)
 F32_OUT_REL = 1e-4        # max |x_hat_gpu - x_hat_ora| <= 1e-4 * max |x_hat_ora|, fp32
 
 
@@ -74,11 +75,29 @@ def kept_admissible(kept_gpu: np.ndarray, s_ora: np.ndarray, k: int, has_cls: bo
     return kept_gpu == ora
 
 
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 values (8 significant bits) in the binade of |v|: the most
+    that rounding a real number to the nearest bf16 value v can move it."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.where(a > 0, 2.0 ** (e - 8), 0.0)
+
+
 def check_block_output(y_gpu: np.ndarray, y_ora: np.ndarray, x_in: np.ndarray, dt: str):
-    d = np.abs(y_gpu.astype(np.float64) - y_ora).max()
+    """bf16: the block's arithmetic error is bounded by 2e-2 * RMS(block input), and the
+    stored output is that result rounded to bf16, so each element may lie a further half
+    bf16 ulp (of its own magnitude) from the oracle's exact value -- for |x_hat| >= 8 at
+    RMS(x) ~ 1.5 that storage rounding alone (up to 2^-5) exceeds the arithmetic bound.
+    fp32: 1e-4 * max |x_hat_ora| (norm-wise relative)."""
+    y = np.asarray(y_gpu, np.float64)
+    err = np.abs(y - y_ora)
     if dt == "bf16":
         tol = BF16_OUT_ABS * float(np.sqrt(np.mean(np.asarray(x_in, np.float64) ** 2)))
+        d = float((err - bf16_half_ulp(y)).max())
+        assert d <= tol, (f"block output err beyond the stored value's half ulp {d:.3e} > {tol:.3e} "
+                          f"(max raw err {err.max():.3e})")
     else:
         tol = F32_OUT_REL * float(np.abs(y_ora).max())
-    assert d <= tol, f"block output max err {d:.3e} > {tol:.3e}"
-    return float(d), tol
+        d = float(err.max())
+        assert d <= tol, f"block output max err {d:.3e} > {tol:.3e}"
+    return d, tol
