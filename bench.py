@@ -34,7 +34,7 @@ METRIC = "img/s (DeiT-S/B) & vid/s (UMT-B/L-shaped) w/ RS pruning, 1 GPU; % roof
 PEAK = {"mfma": 2500.0, "mfma_f32": 157.3, "hbm": 8000.0}
 BREAKDOWN_STEPS = 5   # steps per kernel class in the single-lane breakdown (fc1 and fc2 are close)
 KERNEL_BOUND = {"qkv": "mfma", "attention": "mfma", "proj": "mfma", "fc1": "mfma",
-                "fc2_score": "mfma", "ln_prep": "hbm", "topk": "hbm",
+                "fc2_score": "mfma", "mlp": "mfma", "ln_prep": "hbm", "topk": "hbm",
                 "score": "hbm", "patch_embed": "mfma", "head": "mfma"}
 
 
@@ -87,7 +87,7 @@ def kernel_class(mangled: str):
     if m:
         return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score", "4": "patch_embed",
                 "5": "head"}[m.group(2)]
-    for key, name in (("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
+    for key, name in (("mlp_kernel", "mlp"), ("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
                       ("topk_kernel", "topk"), ("score_kernel", "score"),
                       ("cls_rows_kernel", "patch_embed"), ("pool_partial_kernel", "head"),
                       ("pool_finish_kernel", "head")):
@@ -707,8 +707,8 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the single-lane per-kernel breakdown and every context pass, so "
                          "every launch in the process is a timed-mode launch (for profiler runs)")
-    ap.add_argument("--kernel", default="fc2_score", choices=[k for k in ("ln_prep", "qkv", "attention",
-                    "proj", "fc1", "fc2_score", "topk")],
+    ap.add_argument("--kernel", default="mlp", choices=[k for k in ("ln_prep", "qkv", "attention",
+                    "proj", "fc1", "fc2_score", "mlp", "topk")],
                     help="roofline kernel when --no-breakdown is given")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the Base / Attn / Ours comparison (context)")

@@ -326,7 +326,10 @@ typedef enum {
   RS_KERNEL_PATCH = 9,        /* patch-embedding GEMM and class-token rows */
   RS_KERNEL_HEAD = 10,        /* final LayerNorm + pooling, and the head GEMM */
   RS_KERNEL_MAP_SCORE = 11,   /* Eq. (2) / Eq. (3) scores from the attention kernel's sums */
-  RS_KERNEL_COUNT = 12
+  RS_KERNEL_MLP = 12,         /* the MLP sublayer in one kernel (bf16, C <= 384): LayerNorm 2,
+                                 fc1, GELU, fc2, residual and score partials; replaces
+                                 RS_KERNEL_FC1 + RS_KERNEL_FC2_SCORE for those widths */
+  RS_KERNEL_COUNT = 13
 } rs_kernel_id;
 
 rs_status rs_timing_begin(int kernel_id);
@@ -340,10 +343,13 @@ rs_status rs_timing_end(float* total_ms, int* launches, double* work);
  *      scores: maximum, rescale test, exp2, running sum, bf16 packing of P)
  *   3  16 MFMA 16x16x32 bf16 (the matrix work of that tile)
  *   4  the bodies of 2 and 3 interleaved in one wave on independent registers
+ *   5  8 LDS reads of 16 bytes per lane (1 KiB per wave, contiguous, conflict free)
+ *   6  8 such LDS reads and 8 MFMA 16x16x32 bf16, one fragment per product (the operand
+ *      pattern of the fused MLP kernel's weight fragments)
  * Their rates bound the attention kernel: per tile, the matrix cores need the mode-3 time
  * and the vector units the mode-2 time, and mode 4 shows how far one wave overlaps them.
  * sink: device, workgroups * 256 floats, caller-owned; receives one value per thread so
- * the work is kept.  Asynchronous.  RS_ERR_INVALID_ARG for a mode outside 0..4,
+ * the work is kept.  Asynchronous.  RS_ERR_INVALID_ARG for a mode outside 0..6,
  * workgroups < 1, iters < 1 or a null sink. */
 rs_status rs_probe_throughput(int mode, int workgroups, int iters, float* sink, hipStream_t stream);
 

@@ -153,8 +153,9 @@ def test_workspace_query(N):
     d = _desc(N)
     a = lib.rs_workspace_bytes(ctypes.byref(d), 1, 256, 197)
     b = lib.rs_workspace_bytes(ctypes.byref(d), 12, 256, 197)
-    # activations for one block plus the LayerNorm-folded weights of every block
-    fold = 3 * 384 * 384 * 2
+    # activations for one block plus the LayerNorm-folded weights of every block and, for
+    # the fused MLP kernel (bf16, C <= 384), its packed W1 and W2
+    fold = 3 * 384 * 384 * 2 + 2 * 384 * 1536 * 2
     assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
     assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
     # stored attention maps: B * H * L * pad8(L) elements; Eq. (3) column sums per 64 queries
@@ -279,10 +280,10 @@ def test_attention_noalloc_validation(N):
 
 
 def test_probe_validation(N):
-    """rs_probe_throughput rejects, before any HIP call, a mode outside 0..4, an empty grid or
+    """rs_probe_throughput rejects, before any HIP call, a mode outside 0..6, an empty grid or
     iteration count, and a null sink."""
     lib = N.lib()
-    assert lib.rs_probe_throughput(5, 1024, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
+    assert lib.rs_probe_throughput(7, 1024, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert b"mode" in lib.rs_last_error()
     assert lib.rs_probe_throughput(-1, 1024, 10, FAKE, None) == N.RS_ERR_INVALID_ARG
     assert lib.rs_probe_throughput(0, 0, 10, FAKE, None) == N.RS_ERR_INVALID_ARG

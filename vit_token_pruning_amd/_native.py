@@ -14,7 +14,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rs.h")
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
 KERNELS = ("ln_prep", "qkv", "attention", "proj", "fc1", "fc2_score", "topk", "gather", "score",
-           "patch_embed", "head", "map_score")
+           "patch_embed", "head", "map_score", "mlp")
 RS_POOL_CLS, RS_POOL_MEAN = 0, 1
 
 # field order of rs_embed_weights and of the pointer fields of rs_head_weights

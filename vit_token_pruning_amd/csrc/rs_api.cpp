@@ -172,6 +172,7 @@ struct BlockWs {
 struct FoldWs {   // LayerNorm folding of one block: W_qkv diag(gamma1); c, d of QKV and fc1
   void* wq;
   float *cq, *dq, *c1, *d1;
+  void* wpack;    // the fused MLP kernel's packed W1 / W2 (null when the block runs unfused)
 };
 
 size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
@@ -217,15 +218,20 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
   return off;
 }
 
+rs::Dtype dtype_of(const rs_model_desc& d);
+
 size_t carve_fold(const rs_model_desc& d, char* base, FoldWs* fw) {
   const size_t e = esize(d.dtype), C = d.C, Hd = d.hidden;
-  const size_t sizes[5] = {3 * C * C * e, 3 * C * 4, 3 * C * 4, Hd * 4, Hd * 4};
-  void* p[5];
-  const size_t off = carve_seq(base, sizes, 5, p);
+  const bool fused = rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
+  const size_t sizes[6] = {3 * C * C * e, 3 * C * 4, 3 * C * 4, Hd * 4, Hd * 4,
+                           fused ? rs::mlp_pack_bytes(d.C, d.hidden) : 0};
+  void* p[6];
+  const size_t off = carve_seq(base, sizes, 6, p);
   if (fw) {
     fw->wq = p[0];
     fw->cq = static_cast<float*>(p[1]); fw->dq = static_cast<float*>(p[2]);
     fw->c1 = static_cast<float*>(p[3]); fw->d1 = static_cast<float*>(p[4]);
+    fw->wpack = fused ? p[5] : nullptr;
   }
   return off;
 }
@@ -335,12 +341,28 @@ rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const
       const rs_block_weights& w = blocks[i];
       const FoldWs fw = fold_of(d, ws, i);
       jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, fw.wq, fw.cq, fw.dq, 3 * d.C};
-      jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
-      bytes += (2.0 * 3.0 * d.C + d.hidden) * d.C * esize(d.dtype);
+      // fc1 against LayerNorm 2 (c, d vectors), unless the fused MLP kernel normalises x'
+      // itself
+      const bool fc1_fold = !rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
+      if (fc1_fold) jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
+      bytes += (2.0 * 3.0 * d.C + (fc1_fold ? d.hidden : 0)) * d.C * esize(d.dtype);
     }
     RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
       return rs::launch_fold(dtype_of(d), jobs, nj, d.C, st);
     }));
+  }
+  // the fused MLP kernel's packed weights (same blocks, up to kMaxPackJobs per launch)
+  if (rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden)) {
+    for (int b = b0; b < b0 + n; b += rs::kMaxPackJobs) {
+      rs::MlpPackJob jobs[rs::kMaxPackJobs];
+      int nj = 0;
+      for (int i = b; i < b0 + n && i < b + rs::kMaxPackJobs; ++i)
+        jobs[nj++] = {blocks[i].w_fc1, blocks[i].w_fc2, fold_of(d, ws, i).wpack};
+      const double bytes = 2.0 * nj * rs::mlp_pack_bytes(d.C, d.hidden);
+      RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
+        return rs::launch_mlp_pack(jobs, nj, d.C, d.hidden, st);
+      }));
+    }
   }
   return RS_OK;
 }
@@ -394,36 +416,62 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
       return rs::launch_attention(dt, ws.qkv, ws.o, B, L, d.heads, st);
     }));
   }
+  // The MLP sublayer: one fused kernel (LayerNorm 2, fc1, GELU, fc2, residual, score
+  // partials; the hidden activations stay in registers) where the width allows, else fc1
+  // with LayerNorm 2 folded and fc2 with the score epilogue.
+  const bool fused = rs::mlp_fused_supported(dt, C, Hd);
   {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
-    ep.x = x; ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp; ep.C = C;
-    ep.stats_in = st_x;   // x's row means: fc1's operand is stored as (x' - mean(x)) * gamma2
+    ep.x = x; ep.C = C;
+    if (!fused) {
+      // fc1's operand (x' - mean(x)) * gamma2 and LayerNorm 2's slice partials
+      ep.out2 = ws.xp; ep.gamma = w.ln2_g; ep.stats_out = ws.st_xp;
+      ep.stats_in = st_x;
+    }
     ep.split_ws = ws.split;
     if (part && d.score_op == RS_SHIFT_ATTN) set_score(ep, d, part);   // D(p, x)
     RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
       return rs::launch_gemm(dt, rs::kEpiProj, ws.o, w.w_proj, M, C, C, ep, st);
     }));
   }
-  {
-    rs::GemmEpiArgs ep;
-    ep.out = ws.h; ep.ldo = Hd;
-    ep.stats_in = ws.st_xp; ep.fold_c = fw.c1; ep.fold_d = fw.d1; ep.eps = d.ln_eps; ep.C = C;
-    ep.split_ws = ws.split;
-    RS_HIP(timed(RS_KERNEL_FC1, 2.0 * Md * Cd * Hd, st, [&] {
-      return rs::launch_gemm(dt, rs::kEpiGelu, ws.xp, w.w_fc1, M, Hd, C, ep, st);
+  const bool mlp_scored = part && (d.score_op == RS_SHIFT_MLP || d.score_op == RS_SHIFT_BLOCK);
+  if (fused) {
+    rs::MlpArgs ma;
+    ma.x = x; ma.p = ws.p; ma.ln_g = w.ln2_g; ma.ln_b = w.ln2_b;
+    ma.wpack = fw.wpack; ma.b1 = w.b_fc1; ma.b2 = w.b_fc2;
+    ma.out = out; ma.stats_out = st_out; ma.eps = d.ln_eps;
+    if (mlp_scored) {
+      ma.part = part;
+      ma.nparts = rs::score_parts(C);
+      ma.pstride = (int)part_stride(d);
+      ma.dist = (int)d.score_dist;
+      ma.shift_block = d.score_op == RS_SHIFT_BLOCK;
+    }
+    RS_HIP(timed(RS_KERNEL_MLP, 4.0 * Md * Cd * Hd, st, [&] {
+      return rs::launch_mlp(dt, ma, M, C, Hd, st);
     }));
-  }
-  {
-    rs::GemmEpiArgs ep;
-    ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
-    ep.x = x; ep.p = ws.p;
-    if (part && (d.score_op == RS_SHIFT_MLP || d.score_op == RS_SHIFT_BLOCK)) set_score(ep, d, part);
-    ep.stats_out = st_out; ep.C = C;
-    ep.split_ws = ws.split;
-    RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
-      return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
-    }));
+  } else {
+    {
+      rs::GemmEpiArgs ep;
+      ep.out = ws.h; ep.ldo = Hd;
+      ep.stats_in = ws.st_xp; ep.fold_c = fw.c1; ep.fold_d = fw.d1; ep.eps = d.ln_eps; ep.C = C;
+      ep.split_ws = ws.split;
+      RS_HIP(timed(RS_KERNEL_FC1, 2.0 * Md * Cd * Hd, st, [&] {
+        return rs::launch_gemm(dt, rs::kEpiGelu, ws.xp, w.w_fc1, M, Hd, C, ep, st);
+      }));
+    }
+    {
+      rs::GemmEpiArgs ep;
+      ep.bias = w.b_fc2; ep.out = out; ep.ldo = C;
+      ep.x = x; ep.p = ws.p;
+      if (mlp_scored) set_score(ep, d, part);
+      ep.stats_out = st_out; ep.C = C;
+      ep.split_ws = ws.split;
+      RS_HIP(timed(RS_KERNEL_FC2_SCORE, 2.0 * Md * Cd * Hd, st, [&] {
+        return rs::launch_gemm(dt, rs::kEpiFc2, ws.h, w.w_fc2, M, C, Hd, ep, st);
+      }));
+    }
   }
   if (by_map) {
     // Eq. (2) / Eq. (3) per token into part[0 .. M) (the scores run_select reads)
@@ -1077,7 +1125,7 @@ rs_status rs_vit_forward(const rs_model_desc* desc, const rs_image_desc* img,
 
 rs_status rs_probe_throughput(int mode, int workgroups, int iters, float* sink,
                               hipStream_t stream) {
-  if (mode < 0 || mode > 4) return fail(RS_ERR_INVALID_ARG, "probe mode must be 0 .. 4");
+  if (mode < 0 || mode > 6) return fail(RS_ERR_INVALID_ARG, "probe mode must be 0 .. 6");
   if (workgroups < 1 || iters < 1) return fail(RS_ERR_INVALID_ARG, "workgroups and iters must be >= 1");
   rs_status s;
   if ((s = check_ptr(sink, "sink")) != RS_OK) return s;

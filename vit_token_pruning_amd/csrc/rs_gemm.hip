@@ -179,7 +179,8 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
       for (int e = 0; e < 8; ++e) { c8[e] = ep.fold_c[n + e]; d8[e] = ep.fold_d[n + e]; }
     } else {
       load8f(static_cast<const T*>(ep.bias) + n, b8);
-      if (EPI == kEpiProj) load8f(static_cast<const T*>(ep.gamma) + n, g8);
+      // gamma2 only scales fc1's operand, which is not stored when out2 is null
+      if (EPI == kEpiProj && ep.out2) load8f(static_cast<const T*>(ep.gamma) + n, g8);
     }
   }
 
@@ -274,16 +275,20 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
         // zero mean, so storing (x' - a) * gamma2 in the storage type keeps its precision
         // relative to the row's spread, as storing the normalised row would.
         const float a = kShift ? Rs[mm].x : 0.f;
-        float u[8], pf[8];
+        float pf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pf[e] = v[e] + b8[e];               // attention branch SA(LN(x)) in fp32
           pv[e] = round_t<T>(pf[e]);          // ... as stored
           w[e] = (xv[e] - a) + pv[e];         // x' (Eq. 5) - a in fp32: LayerNorm 2 statistics
-          u[e] = w[e] * g8[e];                // (x' - a) * gamma2: fc1's A operand
         }
         store8f(out + (size_t)m * ep.ldo + n, pv);
-        store8f(static_cast<T*>(ep.out2) + (size_t)m * N + n, u);
+        if (ep.out2) {
+          float u[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) u[e] = w[e] * g8[e];   // (x' - a) * gamma2: fc1's A operand
+          store8f(static_cast<T*>(ep.out2) + (size_t)m * N + n, u);
+        }
         if (ep.part) shift_partials(ep.dist, pf, xv, s0, s1, s2);   // D(SA(LN(x)), x)
       } else if (ep.dist == 0 && !ep.shift_block) {
         // the method: || MLP(LN(x')) - x' ||_2
@@ -324,7 +329,7 @@ __device__ __forceinline__ void tile_epilogue(char* smem, const GemmEpiArgs& ep,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float dd = w[e] - smean;
-      sm2 += dd * dd;
+      sm2 = fmaf(dd, dd, sm2);   // explicit: every statistics producer rounds alike
     }
     sm2 = sum8(sm2);
     if ((sub & 7) == 0 && row_ok && slice < nsl && ep.stats_out) {

@@ -109,6 +109,40 @@ inline int gemm_splits(Dtype dt, int M, int N, int K) {
 hipError_t launch_gemm(Dtype dt, GemmEpilogue epi, const void* A, const void* W, int M, int N,
                        int K, const GemmEpiArgs& ep, hipStream_t stream);
 
+// The MLP sublayer in one kernel (rs_mlp.hip), bf16 and C <= kMlpMaxWidth: LayerNorm 2 of
+// x' = x + p, fc1, GELU, fc2, x_hat = x' + MLP(LN(x')) -> out, and the same score partials
+// (part, as kEpiFc2) and x_hat slice statistics (stats_out) as the fc2 epilogue.  The
+// hidden activations stay in registers.  `out` may alias `x`.
+constexpr int kMlpMaxWidth = 384;
+struct MlpArgs {
+  const void* x = nullptr;      // [M][C] block input
+  const void* p = nullptr;      // [M][C] attention branch (x' = x + p)
+  const void* ln_g = nullptr;   // [C] LayerNorm 2
+  const void* ln_b = nullptr;
+  const void* wpack = nullptr;  // W1 and W2 packed by launch_mlp_pack (mlp_pack_bytes)
+  const void* b1 = nullptr;     // [hidden]
+  const void* b2 = nullptr;     // [C]
+  void* out = nullptr;          // [M][C]
+  float* part = nullptr;        // nullable; layout of GemmEpiArgs::part
+  int nparts = 0, pstride = 0, dist = 0, shift_block = 0;
+  float* stats_out = nullptr;   // nullable; [M][stat_stride(C)] float2
+  float eps = 1e-6f;
+};
+bool mlp_fused_supported(Dtype dt, int C, int hidden);
+hipError_t launch_mlp(Dtype dt, const MlpArgs& a, int M, int C, int hidden, hipStream_t stream);
+// The fused kernel's weight layout: for each 32-unit slice of the hidden layer, the
+// slice's W1 rows then its W2 columns, each as the 1 KiB register fragments of the matrix
+// products in lane order, so every staging load reads 1 KiB of consecutive bytes.  Packed
+// per call (the weights are the caller's, in their own layout) into the workspace.
+inline size_t mlp_pack_bytes(int C, int hidden) { return (size_t)2 * C * hidden * 2; }
+struct MlpPackJob {
+  const void* w1;   // [hidden][C]
+  const void* w2;   // [C][hidden]
+  void* out;        // mlp_pack_bytes(C, hidden)
+};
+constexpr int kMaxPackJobs = 16;
+hipError_t launch_mlp_pack(const MlpPackJob* jobs, int njobs, int C, int hidden, hipStream_t stream);
+
 // Class-token rows of the patch embedding: out[b][0] = cls + pos[0] for b < B (rows of
 // L tokens) and their slice partials stats[b * L].
 hipError_t launch_cls_rows(Dtype dt, const void* cls, const void* pos, void* out, float* stats,

@@ -13,6 +13,11 @@
 //          the rescale test, 16 x (FMA + exp2 + add), the bf16 packing of P
 //  mode 3  16 MFMA 16x16x32 bf16 (the tile's S = K Q^T and O += V^T P^T products)
 //  mode 4  modes 2 and 3 interleaved in one wave on independent registers
+//  mode 5  8 LDS reads of 16 bytes per lane (ds_read_b128; 1 KiB per wave, contiguous in
+//          lane order, conflict free), the operand-fetch pattern of the MLP kernel
+//  mode 6  8 such LDS reads and 8 MFMA 16x16x32 bf16, each product taking one fragment
+//          read in the same iteration (one fragment per product, as the MLP kernel's
+//          weight operands)
 #include "rs_attn_frag.hpp"
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
@@ -60,10 +65,42 @@ __device__ __forceinline__ void softmax_tile(SoftmaxState& st, float scale_log2,
 // One body per mode, each in a loop of its own (so that no branch on the mode sits in
 // the measured loop); returns a value that depends on all of the work.
 template <int MODE>
-__device__ __forceinline__ float probe_body(int iters) {
+__device__ __forceinline__ float probe_body(int iters, const char* lds) {
   const int tid = threadIdx.x;
   const float x0 = (float)(tid & 63) * (1.0f / 64.0f);
   float r = 0.f;
+  if constexpr (MODE == 5 || MODE == 6) {
+    // 16 KiB of LDS in 16 blocks of 1 KiB; iteration it reads blocks (it + i) % 16
+    const char* lb = lds + (tid & 63) * 16;
+    Frag8<bf16> qb;
+    qb.v = u32x4{0x3c003c00u, 0x3c003c00u ^ (uint32_t)tid, 0x3c003c00u, 0x3c003c00u};
+    f32x4 acc[8];
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int off = 0;
+    for (int it = 0; it < iters; ++it) {
+      // the offset is opaque to the compiler (marked changed every iteration), so the
+      // reads are neither hoisted out of the loop nor merged across iterations
+      off ^= 8192;
+      asm volatile("" : "+v"(off));
+      const char* base = lb + off;
+      Frag8<bf16> f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i].v = *reinterpret_cast<const u32x4*>(base + i * 1024);
+      if constexpr (MODE == 5) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x ^= f[i].v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = mma16(acc[i], f[i], qb);
+      }
+    }
+    r = __uint_as_float(x[0] ^ x[1] ^ x[2] ^ x[3]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r += acc[i][0];
+    return r;
+  }
   if constexpr (MODE == 0 || MODE == 1) {
     float x[16];
 #pragma unroll
@@ -113,13 +150,22 @@ __device__ __forceinline__ float probe_body(int iters) {
 }
 
 __global__ __launch_bounds__(256) void probe_kernel(int mode, int iters, float* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) char lds[16384];
+  if (mode >= 5) {
+    // every byte written before it is read
+    for (int i = threadIdx.x; i < 1024; i += 256)
+      reinterpret_cast<u32x4*>(lds)[i] = u32x4{0x3f803f80u ^ (uint32_t)i, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    __syncthreads();
+  }
   float r;
   switch (mode) {
-    case 0: r = probe_body<0>(iters); break;
-    case 1: r = probe_body<1>(iters); break;
-    case 2: r = probe_body<2>(iters); break;
-    case 3: r = probe_body<3>(iters); break;
-    default: r = probe_body<4>(iters); break;
+    case 0: r = probe_body<0>(iters, lds); break;
+    case 1: r = probe_body<1>(iters, lds); break;
+    case 2: r = probe_body<2>(iters, lds); break;
+    case 3: r = probe_body<3>(iters, lds); break;
+    case 4: r = probe_body<4>(iters, lds); break;
+    case 5: r = probe_body<5>(iters, lds); break;
+    default: r = probe_body<6>(iters, lds); break;
   }
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const T* __restrict__ x,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float d = v[e] - mean;
-      m2 += d * d;
+      m2 = fmaf(d, d, m2);   // explicit: every statistics producer rounds alike
     }
     m2 = sum8(m2);
     if ((ch & 7) == 0 && ch < nch) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void cls_rows_kernel(const T* __restrict__ cls
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float d = v[e] - mean;
-      m2 += d * d;
+      m2 = fmaf(d, d, m2);   // explicit: every statistics producer rounds alike
     }
     m2 = sum8(m2);
     if ((ch & 7) == 0 && ch < nch && stats) {
