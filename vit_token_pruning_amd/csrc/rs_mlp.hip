@@ -38,12 +38,7 @@
 namespace rs {
 namespace {
 
-// Token tiles (of 16 rows) per wave: 2 = four waves of 32 rows, one per SIMD, each weight
-// fragment read from LDS feeding two products; 1 = eight waves of 16 rows, two per SIMD.
-#ifndef RS_MLP_TT
-#define RS_MLP_TT 1
-#endif
-constexpr int kMlpRows = 128, kMlpSlice = 32;
+constexpr int kMlpWaves = 8, kMlpRows = 128, kMlpSlice = 32;
 constexpr int kMlpMaxHidden = 4096;   // b1 is kept in LDS (8 KiB)
 
 // The GELU of the bf16 path (same form and constants as the fc1 epilogue of rs_gemm.hip):
@@ -84,38 +79,81 @@ __device__ __forceinline__ Frag8<bf16> lds_frag(const char* p) {
   return f;
 }
 
-template <int NKS, int TT>
-__global__ __launch_bounds__(8 / TT * 64) __attribute__((amdgpu_waves_per_eu(3 - TT, 3 - TT)))
+// EPI: 0 = the method's score, sum (y - x')^2 of the MLP-sublayer shift; 1 = any of the
+// distances and the whole-block shift (runtime choice).
+template <int NKS, int EPI>
+__global__ __launch_bounds__(kMlpWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mlp_kernel(MlpArgs a, int M, int Hd) {
-  constexpr int NW = 8 / TT;           // waves
   constexpr int C = NKS * 32;          // width; NKS = 32-element k steps of fc1
   constexpr int NT = C / 16;           // 16-column output tiles (W2 fragment blocks)
+  constexpr int NJ = C / 32;           // 32-column output groups
   constexpr int W1B = 2 * NKS * 1024;  // staged W1 rows of a slice: (k step, tile) blocks
   constexpr int UNITB = W1B + NT * 1024;
-  constexpr int NLOAD = 4 * NKS / NW;  // fragment blocks each wave loads per unit
-  static_assert(NT * 1024 == W1B && (4 * NKS) % NW == 0, "unit staging layout");
+  constexpr int NLOAD = 4 * NKS / kMlpWaves;   // fragment blocks each wave loads per unit
+  static_assert(NT * 1024 == W1B && (4 * NKS) % kMlpWaves == 0, "unit staging layout");
   __shared__ __attribute__((aligned(16))) char smem[3 * UNITB + kMlpMaxHidden * 2 + C * 2];   // + b1, b2
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int r0 = blockIdx.x * kMlpRows + wave * 16 * TT + l16;   // row of token tile 0
+  const int m = blockIdx.x * kMlpRows + wave * 16 + l16;   // this lane's token row
+  const bool ok = m < M;
+  const size_t mc = (size_t)min(m, M - 1);
   const bf16* x = static_cast<const bf16*>(a.x);
   const bf16* p = static_cast<const bf16*>(a.p);
+  const int NC = Hd / kMlpSlice;
+
+  // ---- staging.  Unit c (LDS buffer c % 3): fragment blocks u < 2 NKS hold slice c + 2's
+  // W1 rows (k step u / 2, row tile u % 2), blocks 2 NKS + j slice c's W2 columns for
+  // output tile j.  Block u of a slice is 1 KiB of the packed weights (lane l's MFMA
+  // operand at 16 l), so each direct load copies 1 KiB of consecutive bytes.  Waves 0-3
+  // load the W1 blocks, waves 4-7 the W2 blocks.  Slices past the end are clamped to the
+  // last one: their blocks are loaded (so every unit is the same NLOAD loads per wave and
+  // the waits below count correctly) but never read.
+  const bool w1side = wave < kMlpWaves / 2;
+  const char* gbase = static_cast<const char*>(a.wpack) + (size_t)wave * NLOAD * 1024 + lane * 16;
+  auto stage = [&](int sc, char* lds_base) {
+    const char* gs = gbase + (size_t)min(sc, NC - 1) * UNITB;
+    char* ls = lds_base + wave * NLOAD * 1024;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) load_lds16(gs + j * 1024, ls + j * 1024);
+  };
+  auto bufp = [&](int c) { return (c % 3) * UNITB; };
+  auto stage_unit = [&](int c) { stage(w1side ? c + 2 : c, smem + bufp(c)); };
+
+  // Prologue loads, in the order they are needed: slices 0 and 1's W1 rows (W1 waves, into
+  // buffer 2), this lane's x and p (LayerNorm 2), b1 / b2 for the LDS tables; units 0 and
+  // 1 after the LayerNorm (the compiler waits for every earlier load before the first use
+  // of x, so loads issued before it would all be waited for).
+  if (w1side) {
+    stage(0, smem + 2 * UNITB);
+    stage(1, smem + 2 * UNITB + W1B);
+  }
+  Frag8<bf16> fx[NKS], fp[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    load_frag(fx[s], x + mc * C + 32 * s + 8 * g);
+    load_frag(fp[s], p + mc * C + 32 * s + 8 * g);
+  }
+  char* btab = smem + 3 * UNITB;
+  char* b2tab = btab + Hd * 2;
+  const int ntab = Hd / 8 + C / 8;                       // 16-byte pieces of b1 then b2
+  const int ti = threadIdx.x;                            // one piece per thread (ntab <= 560)
+  u32x4 tv = u32x4{0u, 0u, 0u, 0u};
+  if (ti < ntab)
+    tv = ti < Hd / 8 ? *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.b1) + ti * 8)
+                     : *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.b2) + (ti - Hd / 8) * 8);
+  u32x4 tv2 = u32x4{0u, 0u, 0u, 0u};
+  const int ti2 = ti + kMlpWaves * 64;
+  if (ti2 < ntab)
+    tv2 = ti2 < Hd / 8 ? *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.b1) + ti2 * 8)
+                       : *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.b2) + (ti2 - Hd / 8) * 8);
 
   // ---- LayerNorm 2 of x' = x + p (Eq. (5)), exact two-pass statistics in fp32 over the
   // row (each token's row is spread over its 4 lanes g = 0..3), one rounding to bf16 of
-  // the normalised, affine row: the fc1 B operand for token tile tt, k-step s, k-group g.
-  Frag8<bf16> xb[TT][NKS];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const size_t mc = (size_t)min(r0 + 16 * tt, M - 1);
-    Frag8<bf16> fx[NKS], fp[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      load_frag(fx[s], x + mc * C + 32 * s + 8 * g);
-      load_frag(fp[s], p + mc * C + 32 * s + 8 * g);
-    }
+  // the normalised, affine row: the fc1 B operand for k-step s, k-group g.
+  Frag8<bf16> xb[NKS];
+  {
     float sum = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -149,134 +187,78 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf(((u[e] + v[e]) - mean) * rstd, gm[e], bt[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xb[tt][s].v[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+      for (int e = 0; e < 4; ++e) xb[s].v[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
     }
-    __builtin_amdgcn_sched_barrier(0);   // one token tile's loads in flight at a time
   }
+  if (ti < ntab) *reinterpret_cast<u32x4*>(btab + ti * 16) = tv;   // b1 then b2, contiguous
+  if (ti2 < ntab) *reinterpret_cast<u32x4*>(btab + ti2 * 16) = tv2;
+  stage_unit(0);
+  stage_unit(1);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- staging.  Unit c (LDS buffer c % 3): fragment blocks u < 2 NKS hold slice c + 2's
-  // W1 rows (k step u / 2, row tile u % 2), blocks 2 NKS + j slice c's W2 columns for
-  // output tile j.  Block u of a slice is 1 KiB of the packed weights (lane l's MFMA
-  // operand at 16 l), so each direct load copies 1 KiB of consecutive bytes.  The first
-  // half of the waves loads the W1 blocks, the second half the W2 blocks.
-  const bool w1side = wave < NW / 2;
-  const char* gbase = static_cast<const char*>(a.wpack) + (size_t)wave * NLOAD * 1024 + lane * 16;
-  // this wave's blocks of slice `sc`'s W1 rows or W2 columns
-  auto stage = [&](int sc, char* lds_base) {
-    const char* gs = gbase + (size_t)sc * UNITB;
-    char* ls = lds_base + wave * NLOAD * 1024;
+  f32x4 acc[NT];
 #pragma unroll
-    for (int j = 0; j < NLOAD; ++j) load_lds16(gs + j * 1024, ls + j * 1024);
-  };
-
-  f32x4 acc[NT][TT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[j][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const bf16* b1 = static_cast<const bf16*>(a.b1);
-  const int NC = Hd / kMlpSlice;
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const char* lb = smem + lane * 16;
-  auto bufp = [&](int c) { return (c % 3) * UNITB; };
+  const char* bl = btab + 16 * g;         // + 64 sc: this lane's 8 b1 values of slice sc
+  auto b1_of = [&](int sc, float* bv) { frag_to_f32(lds_frag(bl + min(sc, NC - 1) * kMlpSlice * 2), bv); };
 
-  // GELU of fc1 + bias, rounded to bf16: the fc2 B operand (k-slots 8 g .. 8 g + 7 =
-  // hidden 8 g + e); h0, h1 hold hidden units 8 g + r and 8 g + 4 + r without the bias.
-  auto gelu = [&](const f32x4& h0, const f32x4& h1, const float* bv) -> Frag8<bf16> {
-    Frag8<bf16> hb;
-    hb.v[0] = pack_bf16x2(mlp_gelu(h0[0] + bv[0]), mlp_gelu(h0[1] + bv[1]));
-    hb.v[1] = pack_bf16x2(mlp_gelu(h0[2] + bv[2]), mlp_gelu(h0[3] + bv[3]));
-    hb.v[2] = pack_bf16x2(mlp_gelu(h1[0] + bv[4]), mlp_gelu(h1[1] + bv[5]));
-    hb.v[3] = pack_bf16x2(mlp_gelu(h1[2] + bv[6]), mlp_gelu(h1[3] + bv[7]));
-    return hb;
-  };
   // fc1 of one slice alone, from the W1 blocks at `w1s` (prologue)
-  auto fc1 = [&](const char* w1s, f32x4* h0, f32x4* h1) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) h0[tt] = h1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fc1 = [&](const char* w1s, f32x4& h0, f32x4& h1) {
+    h0 = h1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const Frag8<bf16> f0 = lds_frag(w1s + (2 * s) * 1024), f1 = lds_frag(w1s + (2 * s + 1) * 1024);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        h0[tt] = mma16(h0[tt], f0, xb[tt][s]);
-        h1[tt] = mma16(h1[tt], f1, xb[tt][s]);
-      }
-    }
-  };
-  auto fc2 = [&](const char* w2s, const Frag8<bf16>* hb) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const Frag8<bf16> f = lds_frag(w2s + j * 1024);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[j][tt] = mma16(acc[j][tt], f, hb[tt]);
+      h0 = mma16(h0, lds_frag(w1s + (2 * s) * 1024), xb[s]);
+      h1 = mma16(h1, lds_frag(w1s + (2 * s + 1) * 1024), xb[s]);
     }
   };
 
   // Pipeline: iteration c runs fc2 of slice c, GELU of slice c + 1 and fc1 of slice
   // c + 2 -- three independent streams -- reading unit c (W1 of c + 2, W2 of c), while
-  // units c + 1 and c + 2 load.  Prologue: slices 0 and 1's W1 rows (buffer 2), units 0
-  // and 1 (buffers 0 and 1).
-  Frag8<bf16> hbuf[TT];                   // GELU output of slice c: the fc2 B operand
-  f32x4 hp0[TT], hp1[TT];                 // fc1 of slice c + 1 (no bias)
-  // b1 in LDS (read with the fragments: no global load inside the slice loop, whose
-  // direct-to-LDS loads would otherwise make the compiler wait for all of them)
-  char* btab = smem + 3 * UNITB;
-  for (int i = threadIdx.x; i < Hd / 8; i += NW * 64)
-    *reinterpret_cast<u32x4*>(btab + i * 16) = *reinterpret_cast<const u32x4*>(b1 + i * 8);
-  char* b2tab = btab + kMlpMaxHidden * 2;  // b2 for the epilogue
-  for (int i = threadIdx.x; i < C / 8; i += NW * 64)
-    *reinterpret_cast<u32x4*>(b2tab + i * 16) =
-        *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.b2) + i * 8);
-  const char* bl = btab + 16 * g;         // + 64 sc: this lane's 8 b1 values of slice sc
+  // units c + 1 and c + 2 load.  The last two iterations run on clamped slices whose fc1
+  // and GELU results are not used, so every iteration is the same pinned sequence.
+  Frag8<bf16> hbuf;                       // GELU output of slice c: the fc2 B operand
+  f32x4 hp0, hp1;                         // fc1 of slice c + 1 (no bias)
+  wait_vmem<2 * NLOAD>();                 // W1 waves: slices 0 and 1 staged (units 0, 1 may not be)
+  // the b1 / b2 table writes done, then every wave (no fence: __syncthreads() would also
+  // wait for units 0 and 1)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   {
-    if (w1side) {
-      stage(0, smem + 2 * UNITB);         // W1 blocks of slice 0, and of slice 1 in the W2 half
-      stage(1, smem + 2 * UNITB + W1B);
-    }
-    // units 0 and 1 (W1 of slices 2, 3 clamped: past the end they are never read)
-    stage(w1side ? min(2, NC - 1) : 0, smem);
-    stage(w1side ? min(3, NC - 1) : 1, smem + UNITB);
-    wait_vmem<0>();
-    __syncthreads();                      // the b1 table too
-    f32x4 t0[TT], t1[TT];
+    f32x4 t0, t1;
     fc1(lb + 2 * UNITB, t0, t1);
     float bv[8];
-    frag_to_f32(lds_frag(bl), bv);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) hbuf[tt] = gelu(t0[tt], t1[tt], bv);
+    b1_of(0, bv);
+    hbuf.v[0] = pack_bf16x2(mlp_gelu(t0[0] + bv[0]), mlp_gelu(t0[1] + bv[1]));
+    hbuf.v[1] = pack_bf16x2(mlp_gelu(t0[2] + bv[2]), mlp_gelu(t0[3] + bv[3]));
+    hbuf.v[2] = pack_bf16x2(mlp_gelu(t1[0] + bv[4]), mlp_gelu(t1[1] + bv[5]));
+    hbuf.v[3] = pack_bf16x2(mlp_gelu(t1[2] + bv[6]), mlp_gelu(t1[3] + bv[7]));
     fc1(lb + 2 * UNITB + W1B, hp0, hp1);  // slice 1's fc1
   }
 
-  // One iteration's matrix work as one straight sequence of 4 NKS slots, each one
-  // fragment read from LDS and TT products with it: even slots are fc1 of slice c + 2
-  // (step q / 4, tile (q / 2) % 2), odd slots fc2 of slice c (output tile q / 2).  Each
-  // slot's fragment is read kDepth slots ahead, and the GELU of slice c + 1 is spread
-  // over the slots.  Scheduling barriers between slots keep that order: left to itself
-  // the compiler moves each fragment read next to its product, and the wave then waits on
-  // LDS at almost every product.  The next unit's loads are issued after the slots
-  // (direct-to-LDS loads issued among the fragment reads make the compiler wait for every
-  // outstanding LDS read at each product).
-  constexpr int NQ = 4 * NKS, kDepth = 6, NG = 8 * TT;   // slots, read-ahead, GELUs
-  int c = 0;
-  for (; c + 2 < NC; ++c) {
+  // One iteration's matrix work as one straight sequence of 4 NKS slots, each one fragment
+  // read from LDS and one product with it: even slots are fc1 of slice c + 2 (step q / 4,
+  // tile (q / 2) % 2), odd slots fc2 of slice c (output tile q / 2).  Each slot's fragment
+  // is read kDepth slots ahead, and the GELU of slice c + 1 is spread over the slots.
+  // Scheduling barriers between slots keep that order: left to itself the compiler moves
+  // each fragment read next to its product, and the wave then waits on LDS at almost every
+  // product.  The next unit's loads are issued after the slots (direct-to-LDS loads issued
+  // among the fragment reads make the compiler wait for every outstanding LDS read at each
+  // product).
+  constexpr int NQ = 4 * NKS, kDepth = 6;
+  for (int c = 0; c < NC; ++c) {
     wait_vmem<NLOAD>();  // this wave's blocks of unit c have landed (unit c + 1 may not)
     barrier_nofence();   // ... and every wave's; unit c - 1's buffer is no longer read
     const char* us = lb + bufp(c);
     auto faddr = [&](int q) { return us + ((q & 1) ? W1B + (q >> 1) * 1024 : (q >> 1) * 1024); };
-    f32x4 h0[TT], h1[TT];
-    float gl[NG], gv[NG];
+    f32x4 h0 = f32x4{0.f, 0.f, 0.f, 0.f}, h1 = h0;
+    float gl[8], gv[8];
     {
       float bv[8];
-      frag_to_f32(lds_frag(bl + (c + 1) * kMlpSlice * 2), bv);   // b1 of slice c + 1
+      b1_of(c + 1, bv);
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        h0[tt] = h1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          gl[8 * tt + e] = hp0[tt][e] + bv[e];
-          gl[8 * tt + 4 + e] = hp1[tt][e] + bv[4 + e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        gl[e] = hp0[e] + bv[e];
+        gl[4 + e] = hp1[e] + bv[4 + e];
       }
     }
     Frag8<bf16> f[kDepth];
@@ -287,115 +269,80 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
     for (int q = 0; q < NQ; ++q) {
       const Frag8<bf16> cur = f[q % kDepth];
       if (q + kDepth < NQ) f[q % kDepth] = lds_frag(faddr(q + kDepth));
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        if (q & 1) {
-          acc[q >> 1][tt] = mma16(acc[q >> 1][tt], cur, hbuf[tt]);
-        } else if ((q >> 1) & 1) {
-          h1[tt] = mma16(h1[tt], cur, xb[tt][q >> 2]);
-        } else {
-          h0[tt] = mma16(h0[tt], cur, xb[tt][q >> 2]);
-        }
+      if (q & 1) {
+        acc[q >> 1] = mma16(acc[q >> 1], cur, hbuf);
+      } else if ((q >> 1) & 1) {
+        h1 = mma16(h1, cur, xb[q >> 2]);
+      } else {
+        h0 = mma16(h0, cur, xb[q >> 2]);
       }
       // GELU element i at slots spread evenly over the iteration
 #pragma unroll
-      for (int i = 0; i < NG; ++i)
-        if ((i * NQ) / NG == q) gv[i] = mlp_gelu(gl[i]);
+      for (int i = 0; i < 8; ++i)
+        if ((i * NQ) / 8 == q) gv[i] = mlp_gelu(gl[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hbuf[tt].v[e] = pack_bf16x2(gv[8 * tt + 2 * e], gv[8 * tt + 2 * e + 1]);
-      hp0[tt] = h0[tt];
-      hp1[tt] = h1[tt];
-    }
-    // unit c + 2: slice c + 4's W1 rows (clamped past the end, then never read) and slice
-    // c + 2's W2 columns, into the buffer unit c - 1 used
-    stage(w1side ? min(c + 4, NC - 1) : c + 2, smem + bufp(c + 2));
+    for (int e = 0; e < 4; ++e) hbuf.v[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+    hp0 = h0;
+    hp1 = h1;
+    stage_unit(c + 2);   // into the buffer unit c - 1 used
   }
-  // the last two slices: fc2 of NC - 2 with GELU of NC - 1, then fc2 of NC - 1
-  wait_vmem<NLOAD>();
-  barrier_nofence();
-  // the epilogue's x and p, requested now so that they arrive during the last two slices
-  constexpr int NJ = C / 32;
-  Frag8<bf16> ex[TT][NJ], epv[TT][NJ];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const size_t mc = (size_t)min(r0 + 16 * tt, M - 1);
-#pragma unroll
-    for (int J = 0; J < NJ; ++J) {
-      load_frag(ex[tt][J], x + mc * C + 32 * J + 8 * g);
-      load_frag(epv[tt][J], p + mc * C + 32 * J + 8 * g);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    float bv[8];
-    frag_to_f32(lds_frag(bl + (c + 1) * kMlpSlice * 2), bv);
-    Frag8<bf16> hn[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) hn[tt] = gelu(hp0[tt], hp1[tt], bv);
-    fc2(lb + bufp(c) + W1B, hbuf);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) hbuf[tt] = hn[tt];
-  }
-  ++c;
-  wait_vmem<2 * TT * NJ>();   // unit NC - 1 (older than the epilogue's loads) has landed
-  barrier_nofence();
-  fc2(lb + bufp(c) + W1B, hbuf);
 
-  // ---- epilogue: acc[2 J + t][tt][r] = y - b2 of row r0 + 16 tt, output column
-  // 32 J + 8 g + 4 t + r.  y = MLP(LN(x')); x' = x + p re-formed in fp32; x_hat = x' + y
-  // stored; the shift partials and the stored row's statistics per 64-column slice
-  // (J = 2 sl, 2 sl + 1), summed over the token's 4 lanes.
+  // ---- epilogue: acc[2 J + t][r] = y - b2 of row m, output column 32 J + 8 g + 4 t + r.
+  // y = MLP(LN(x')); x' = x + p re-formed in fp32; x_hat = x' + y stored; the shift
+  // partials and the stored row's statistics per 64-column slice (J = 2 sl, 2 sl + 1),
+  // summed over the token's 4 lanes.  x and p of slice sl + 1 are requested before slice sl
+  // is computed.
   const int nsl = C / 64, sstride = stat_stride(C);
   bf16* out = static_cast<bf16*>(a.out);
+  Frag8<bf16> ex[2][2], epp[2][2];        // [buffer][J within the slice]
+  auto load_slice = [&](int sl, int b) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int m = r0 + 16 * tt;
-    const bool ok = m < M;
-    const size_t mc = (size_t)min(m, M - 1);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int n = 64 * sl + 32 * h2 + 8 * g;
+      load_frag(ex[b][h2], x + mc * C + n);
+      load_frag(epp[b][h2], p + mc * C + n);
+    }
+  };
+  load_slice(0, 0);
 #pragma unroll
-    for (int sl = 0; sl < nsl; ++sl) {
-      float w[16], s0 = 0.f, s1 = 0.f, s2 = 0.f, cs[2] = {0.f, 0.f};
+  for (int sl = 0; sl < nsl; ++sl) {
+    if (sl + 1 < nsl) load_slice(sl + 1, (sl + 1) & 1);
+    float w[16], s0 = 0.f, s1 = 0.f, s2 = 0.f, cs[2] = {0.f, 0.f};
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int J = 2 * sl + h2, n = 32 * J + 8 * g;
-        float xv[8], pv[8], bb[8], y[8], fa[8], fb[8];
-        frag_to_f32(ex[tt][J], xv);
-        frag_to_f32(epv[tt][J], pv);
-        frag_to_f32(lds_frag(b2tab + n * 2), bb);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int J = 2 * sl + h2, n = 32 * J + 8 * g;
+      float xv[8], pv[8], bb[8];
+      frag_to_f32(ex[sl & 1][h2], xv);
+      frag_to_f32(epp[sl & 1][h2], pv);
+      frag_to_f32(lds_frag(b2tab + n * 2), bb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          y[e] = acc[2 * J + (e >> 2)][tt][e & 3] + bb[e];   // MLP(LN(x'))
-          const float xp = xv[e] + pv[e];                      // x' (Eq. (5)) in fp32
-          w[8 * h2 + e] = round_t<bf16>(xp + y[e]);            // x_hat (Eq. (6)), as stored
-          fa[e] = a.shift_block ? xp + y[e] : y[e];            // x_hat | MLP(LN(x'))
-          fb[e] = a.shift_block ? xv[e] : xp;                  // x     | x'
-          cs[h2] += w[8 * h2 + e];                             // this 8-column chunk's sum
-        }
-        if (ok) store8f(out + mc * C + n, w + 8 * h2);
-        if (a.part) {
+      for (int e = 0; e < 8; ++e) {
+        const float y = acc[2 * J + (e >> 2)][e & 3] + bb[e];   // MLP(LN(x'))
+        const float xp = xv[e] + pv[e];                          // x' (Eq. (5)) in fp32
+        w[8 * h2 + e] = round_t<bf16>(xp + y);                   // x_hat (Eq. (6)), as stored
+        cs[h2] += w[8 * h2 + e];                                 // this 8-column chunk's sum
+        if (EPI == 0) {
+          const float d = y - xp;
+          s0 = fmaf(d, d, s0);
+        } else {
+          const float fa = a.shift_block ? xp + y : y;            // x_hat | MLP(LN(x'))
+          const float fb = a.shift_block ? xv[e] : xp;            // x     | x'
           if (a.dist == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float d = fa[e] - fb[e];
-              s0 += d * d;
-            }
+            s0 = fmaf(fa - fb, fa - fb, s0);
           } else if (a.dist == 1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s0 += fabsf(fa[e] - fb[e]);
+            s0 += fabsf(fa - fb);
           } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              s0 += fa[e] * fb[e];
-              s1 += fa[e] * fa[e];
-              s2 += fb[e] * fb[e];
-            }
+            s0 = fmaf(fa, fb, s0);
+            s1 = fmaf(fa, fa, s1);
+            s2 = fmaf(fb, fb, s2);
           }
         }
       }
+      if (ok) store8f(out + mc * C + n, w + 8 * h2);
+    }
+    if (a.stats_out) {
       // slice statistics of the stored row in the row statistics kernel's order:
       // sequential within each 8-column chunk (chunk g of J = 2 sl, chunk 4 + g of
       // J = 2 sl + 1), then ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7))
@@ -409,33 +356,35 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
           cm[h2] = fmaf(d, d, cm[h2]);
         }
       const float sm2 = sum_groups(cm[0]) + sum_groups(cm[1]);
-      if (a.stats_out && ok && g == 0) {
+      if (ok && g == 0) {
         float* so = a.stats_out + (mc * sstride + sl) * 2;
         so[0] = smean;
         so[1] = sm2;
       }
-      if (a.part) {
-        s0 = sum_groups(s0);
-        if (a.dist == 2) {
-          s1 = sum_groups(s1);
-          s2 = sum_groups(s2);
-        }
-        if (ok && g == 0) {
-          float* pr = a.part + mc * a.pstride + sl;
-          pr[0] = s0;
-          if (a.dist == 2) {
-            pr[a.nparts] = s1;
-            pr[2 * a.nparts] = s2;
-          }
+    }
+    if (a.part) {
+      s0 = sum_groups(s0);
+      if (EPI == 1 && a.dist == 2) {
+        s1 = sum_groups(s1);
+        s2 = sum_groups(s2);
+      }
+      if (ok && g == 0) {
+        float* pr = a.part + mc * a.pstride + sl;
+        pr[0] = s0;
+        if (EPI == 1 && a.dist == 2) {
+          pr[a.nparts] = s1;
+          pr[2 * a.nparts] = s2;
         }
       }
     }
-    // partial slots past the last 64-column slice (the score reads nparts per quantity)
-    if (a.part && ok && g == 0) {
-      for (int q = 0; q < (a.dist == 2 ? 3 : 1); ++q)
-        for (int sl = nsl; sl < a.nparts; ++sl) a.part[mc * a.pstride + q * a.nparts + sl] = 0.f;
-    }
+    __builtin_amdgcn_sched_barrier(0);   // one slice's loads ahead, not all of them
   }
+  // partial slots past the last 64-column slice (the score reads nparts per quantity)
+  if (a.part && ok && g == 0) {
+    for (int q = 0; q < (a.dist == 2 ? 3 : 1); ++q)
+      for (int sl = nsl; sl < a.nparts; ++sl) a.part[mc * a.pstride + q * a.nparts + sl] = 0.f;
+  }
+  wait_vmem<0>();   // the two clamped units' direct-to-LDS loads have landed before the LDS is freed
 }
 
 // Packing of W1 / W2 into the fused kernel's fragment order: 16-byte chunk i of a block's
@@ -470,7 +419,11 @@ __global__ __launch_bounds__(256) void mlp_pack_kernel(MlpPackArgs pa) {
 
 template <int NKS>
 hipError_t launch_nks(const MlpArgs& a, int M, int hidden, hipStream_t st) {
-  mlp_kernel<NKS, RS_MLP_TT><<<(M + kMlpRows - 1) / kMlpRows, 8 / RS_MLP_TT * 64, 0, st>>>(a, M, hidden);
+  const int grid = (M + kMlpRows - 1) / kMlpRows;
+  if (a.part && (a.dist != 0 || a.shift_block))
+    mlp_kernel<NKS, 1><<<grid, kMlpWaves * 64, 0, st>>>(a, M, hidden);
+  else
+    mlp_kernel<NKS, 0><<<grid, kMlpWaves * 64, 0, st>>>(a, M, hidden);
   return hipGetLastError();
 }
 
