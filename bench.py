@@ -238,7 +238,10 @@ def summarize_trace(dirs):
     lines.append("Symbols:")
     lines.append("")
     for kc in sorted(names):
-        lines.append(f"- {kc}: `{names[kc].split('(')[0] if not names[kc].startswith('_Z') else names[kc]}`")
+        nm = names[kc]
+        if not nm.startswith("_Z") and nm.endswith(")"):
+            nm = nm[:nm.rfind("(")]   # demangled: drop the argument list only
+        lines.append(f"- {kc}: `{nm}`")
     return "\n".join(lines)
 
 
