@@ -87,7 +87,12 @@ def kernel_class(mangled: str):
     if m:
         return {"0": "qkv", "1": "proj", "2": "fc1", "3": "fc2_score", "4": "patch_embed",
                 "5": "head"}[m.group(2)]
-    for key, name in (("mlp_kernel", "mlp"), ("attention_kernel", "attention"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
+    # the weight-streaming linear kernel: with LayerNorm 1 (template flag true) the QKV
+    # projection, without it the attention projection
+    m = re.search(r"lin_kernelILi\d+ELb([01])E", mangled)
+    if m:
+        return "qkv" if m.group(1) == "1" else "proj"
+    for key, name in (("mlp_kernel", "mlp"), ("attention_kernel", "attention"), ("pack_kernel", "ln_prep"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
                       ("topk_kernel", "topk"), ("score_kernel", "score"),
                       ("cls_rows_kernel", "patch_embed"), ("pool_partial_kernel", "head"),
                       ("pool_finish_kernel", "head")):

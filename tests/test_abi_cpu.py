@@ -153,9 +153,10 @@ def test_workspace_query(N):
     d = _desc(N)
     a = lib.rs_workspace_bytes(ctypes.byref(d), 1, 256, 197)
     b = lib.rs_workspace_bytes(ctypes.byref(d), 12, 256, 197)
-    # activations for one block plus the LayerNorm-folded weights of every block and, for
-    # the fused MLP kernel (bf16, C <= 384), its packed W1 and W2
-    fold = 3 * 384 * 384 * 2 + 2 * 384 * 1536 * 2
+    # activations for one block plus the per-call weights of every block: W_qkv (folded,
+    # or packed for the weight-streaming kernel), and for bf16 at C <= 384 the fused MLP
+    # kernel's packed W1 and W2 and the packed W_proj
+    fold = 3 * 384 * 384 * 2 + 2 * 384 * 1536 * 2 + 384 * 384 * 2
     assert a % 256 == 0 and a > 256 * 197 * 384 * 2 * 8
     assert b - a >= 11 * fold and b - a < 11 * (fold + 64 * 1024)
     # stored attention maps: B * H * L * pad8(L) elements; Eq. (3) column sums per 64 queries

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librs.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-DEVICE_SOURCES = ["rs_gemm.hip", "rs_mlp.hip", "rs_attn.hip", "rs_attn_map.hip", "rs_rowops.hip", "rs_noalloc.hip", "rs_probe.hip"]
+DEVICE_SOURCES = ["rs_gemm.hip", "rs_mlp.hip", "rs_lin.hip", "rs_attn.hip", "rs_attn_map.hip", "rs_rowops.hip", "rs_noalloc.hip", "rs_probe.hip"]
 HOST_SOURCES = ["rs_api.cpp"]
 
 HIP_FLAGS = [

@@ -170,9 +170,10 @@ struct BlockWs {
   float* mapsum;  // Eq. (2) rows [B][H][L] or Eq. (3) column sums [B][H][nq][L] (map scores)
 };
 struct FoldWs {   // LayerNorm folding of one block: W_qkv diag(gamma1); c, d of QKV and fc1
-  void* wq;
+  void* wq;       // (weight-streaming QKV: W_qkv packed for that kernel instead)
   float *cq, *dq, *c1, *d1;
   void* wpack;    // the fused MLP kernel's packed W1 / W2 (null when the block runs unfused)
+  void* ppack;    // W_proj packed for the weight-streaming kernel (null when not used)
 };
 
 size_t carve_seq(char* base, const size_t* sizes, int n, void** ptrs) {
@@ -220,18 +221,35 @@ size_t carve_block(const rs_model_desc& d, int B, int L, char* base, BlockWs* ws
 
 rs::Dtype dtype_of(const rs_model_desc& d);
 
+#ifndef RS_USE_LIN
+#define RS_USE_LIN 3
+#endif
+// The QKV projection runs on the weight-streaming kernel (LayerNorm 1 in the kernel, W_qkv
+// packed per call) where it supports the width; the attention projection too when the MLP
+// sublayer is fused (the unfused fc1 needs the projection's LayerNorm-2 epilogue).
+bool lin_qkv(const rs_model_desc& d) {
+  return (RS_USE_LIN & 1) && rs::lin_supported(dtype_of(d), d.C, 3 * d.C);
+}
+bool lin_proj_packed(const rs_model_desc& d) {
+  return (RS_USE_LIN & 2) && rs::lin_supported(dtype_of(d), d.C, d.C) &&
+         rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
+}
+
 size_t carve_fold(const rs_model_desc& d, char* base, FoldWs* fw) {
   const size_t e = esize(d.dtype), C = d.C, Hd = d.hidden;
   const bool fused = rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
-  const size_t sizes[6] = {3 * C * C * e, 3 * C * 4, 3 * C * 4, Hd * 4, Hd * 4,
-                           fused ? rs::mlp_pack_bytes(d.C, d.hidden) : 0};
-  void* p[6];
-  const size_t off = carve_seq(base, sizes, 6, p);
+  const bool pp = lin_proj_packed(d);
+  const size_t sizes[7] = {3 * C * C * e, 3 * C * 4, 3 * C * 4, Hd * 4, Hd * 4,
+                           fused ? rs::mlp_pack_bytes(d.C, d.hidden) : 0,
+                           pp ? rs::lin_pack_bytes(d.C, d.C) : 0};
+  void* p[7];
+  const size_t off = carve_seq(base, sizes, 7, p);
   if (fw) {
     fw->wq = p[0];
     fw->cq = static_cast<float*>(p[1]); fw->dq = static_cast<float*>(p[2]);
     fw->c1 = static_cast<float*>(p[3]); fw->d1 = static_cast<float*>(p[4]);
     fw->wpack = fused ? p[5] : nullptr;
+    fw->ppack = pp ? p[6] : nullptr;
   }
   return off;
 }
@@ -340,16 +358,42 @@ rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const
     for (int i = b; i < b0 + n && i < b + rs::kMaxFoldJobs / 2; ++i) {
       const rs_block_weights& w = blocks[i];
       const FoldWs fw = fold_of(d, ws, i);
-      jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, fw.wq, fw.cq, fw.dq, 3 * d.C};
+      // QKV against LayerNorm 1 (the weight-streaming kernel takes W_qkv diag(gamma1)
+      // packed in its own layout, below, and only the folded bias d from here)
+      const bool qkv_fold = !lin_qkv(d);
+      jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, qkv_fold ? fw.wq : nullptr, fw.cq, fw.dq, 3 * d.C};
       // fc1 against LayerNorm 2 (c, d vectors), unless the fused MLP kernel normalises x'
       // itself
       const bool fc1_fold = !rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
       if (fc1_fold) jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
-      bytes += (2.0 * 3.0 * d.C + (fc1_fold ? d.hidden : 0)) * d.C * esize(d.dtype);
+      bytes += ((qkv_fold ? 2.0 : 1.0) * 3.0 * d.C + (fc1_fold ? d.hidden : 0)) * d.C * esize(d.dtype);
     }
     RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
       return rs::launch_fold(dtype_of(d), jobs, nj, d.C, st);
     }));
+  }
+  // the weight-streaming kernel's packed W_qkv and W_proj
+  if (lin_qkv(d) || lin_proj_packed(d)) {
+    const bool pq = lin_qkv(d), pp = lin_proj_packed(d);
+    for (int b = b0; b < b0 + n; b += rs::kMaxLinPackJobs / 2) {
+      rs::LinPackJob jobs[rs::kMaxLinPackJobs];
+      int nj = 0;
+      double bytes = 0.0;
+      for (int i = b; i < b0 + n && i < b + rs::kMaxLinPackJobs / 2; ++i) {
+        const FoldWs fw = fold_of(d, ws, i);
+        if (pq) {
+          jobs[nj++] = {blocks[i].w_qkv, blocks[i].ln1_g, fw.wq, 3 * d.C};
+          bytes += 2.0 * rs::lin_pack_bytes(d.C, 3 * d.C);
+        }
+        if (pp) {
+          jobs[nj++] = {blocks[i].w_proj, nullptr, fw.ppack, d.C};
+          bytes += 2.0 * rs::lin_pack_bytes(d.C, d.C);
+        }
+      }
+      RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
+        return rs::launch_lin_pack(jobs, nj, d.C, st);
+      }));
+    }
   }
   // the fused MLP kernel's packed weights (same blocks, up to kMaxPackJobs per launch)
   if (rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden)) {
@@ -394,7 +438,14 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
   const rs::Dtype dt = dtype_of(d);
   const int M = B * L, C = d.C, Hd = d.hidden;
   const double Md = M, Cd = C;
-  {
+  if (lin_qkv(d)) {
+    rs::LinArgs la;
+    la.a = x; la.stats = st_x; la.wpack = fw.wq; la.bias_f = fw.dq;
+    la.out = ws.qkv; la.ldo = 3 * C; la.eps = d.ln_eps;
+    RS_HIP(timed(RS_KERNEL_QKV, 2.0 * Md * 3 * Cd * Cd, st, [&] {
+      return rs::launch_lin(dt, la, M, C, 3 * C, st);
+    }));
+  } else {
     rs::GemmEpiArgs ep;
     ep.out = ws.qkv; ep.ldo = 3 * C;
     ep.stats_in = st_x; ep.fold_c = fw.cq; ep.fold_d = fw.dq; ep.eps = d.ln_eps; ep.C = C;
@@ -420,7 +471,14 @@ rs_status run_block(const rs_model_desc& d, const rs_block_weights& w, const Fol
   // partials; the hidden activations stay in registers) where the width allows, else fc1
   // with LayerNorm 2 folded and fc2 with the score epilogue.
   const bool fused = rs::mlp_fused_supported(dt, C, Hd);
-  {
+  if (fw.ppack && !(part && d.score_op == RS_SHIFT_ATTN)) {
+    // p alone (no epilogue work): the weight-streaming kernel
+    rs::LinArgs la;
+    la.a = ws.o; la.wpack = fw.ppack; la.bias = w.b_proj; la.out = ws.p; la.ldo = C;
+    RS_HIP(timed(RS_KERNEL_PROJ, 2.0 * Md * Cd * Cd, st, [&] {
+      return rs::launch_lin(dt, la, M, C, C, st);
+    }));
+  } else {
     rs::GemmEpiArgs ep;
     ep.bias = w.b_proj; ep.out = ws.p; ep.ldo = C;
     ep.x = x; ep.C = C;

@@ -21,8 +21,8 @@ inline int score_parts(int C) { return 2 * ((C + kGemmTile - 1) / kGemmTile); }
 // Row statistics travel as partials over 64-column slices: (slice mean, slice sum of squared
 // deviations from it), merged exactly by the consumer.  A row of partials is padded to an
 // even number of slices (16-byte rows).
-__host__ __device__ inline int stat_slices(int C) { return C / 64; }
-__host__ __device__ inline int stat_stride(int C) { return (C / 64 + 1) / 2 * 2; }  // float2 per row
+__host__ __device__ constexpr int stat_slices(int C) { return C / 64; }
+__host__ __device__ constexpr int stat_stride(int C) { return (C / 64 + 1) / 2 * 2; }  // float2 per row
 
 enum GemmEpilogue {
   kEpiQKV = 0,   // LN1 folded; Q|K|V -> qkv [M][3C]
@@ -142,6 +142,38 @@ struct MlpPackJob {
 };
 constexpr int kMaxPackJobs = 16;
 hipError_t launch_mlp_pack(const MlpPackJob* jobs, int njobs, int C, int hidden, hipStream_t stream);
+
+// Weight-streaming linear layer (rs_lin.hip), bf16, K = C <= kMlpMaxWidth, N <= kLinMaxN:
+// out[m][n] = A'[m] . W'[n] + b'[n].  With `stats` (the rows' slice partials, as
+// GemmEpiArgs::stats_in), A' = (A row - mean) * rstd rounded to bf16, W' = W diag(gamma)
+// (packed with gamma) and b' = bias_f (fp32: b + W beta), i.e. LayerNorm(A) W^T + b;
+// without, A' = A, W' = W and b' = bias (bf16).  The QKV projection with LayerNorm 1 and
+// the attention output projection.
+constexpr int kLinMaxN = 1536;
+struct LinArgs {
+  const void* a = nullptr;      // [M][K]
+  const float* stats = nullptr; // [M][stat_stride(K)] float2, or null (no LayerNorm)
+  const void* wpack = nullptr;  // W packed by launch_lin_pack (lin_pack_bytes)
+  const void* bias = nullptr;   // [N] bf16 (no LayerNorm)
+  const float* bias_f = nullptr;// [N] fp32 (LayerNorm)
+  void* out = nullptr;          // [M][ldo]
+  int ldo = 0;
+  float eps = 1e-6f;
+};
+bool lin_supported(Dtype dt, int K, int N);
+hipError_t launch_lin(Dtype dt, const LinArgs& a, int M, int K, int N, hipStream_t stream);
+// W [N][K] (times diag(gamma) when given, rounded to bf16) in the kernel's layout: per
+// 32-row slice of W, its 1 KiB MFMA register fragments in lane order (rows permuted within
+// the slice so that each lane's eight results are eight consecutive output columns).
+inline size_t lin_pack_bytes(int K, int N) { return (size_t)K * N * 2; }
+struct LinPackJob {
+  const void* w;      // [N][K]
+  const void* gamma;  // [K] or null
+  void* out;          // lin_pack_bytes(K, N)
+  int N;
+};
+constexpr int kMaxLinPackJobs = 16;
+hipError_t launch_lin_pack(const LinPackJob* jobs, int njobs, int K, hipStream_t stream);
 
 // Class-token rows of the patch embedding: out[b][0] = cls + pos[0] for b < B (rows of
 // L tokens) and their slice partials stats[b * L].
