@@ -89,9 +89,9 @@ def kernel_class(mangled: str):
                 "5": "head"}[m.group(2)]
     # the weight-streaming linear kernel: with LayerNorm 1 (template flag true) the QKV
     # projection, without it the attention projection
-    m = re.search(r"lin_kernelILi\d+ELb([01])E", mangled)
+    m = re.search(r"lin_kernel(?:ILi\d+ELb([01])E|<\d+, (true|false)>)", mangled)
     if m:
-        return "qkv" if m.group(1) == "1" else "proj"
+        return "qkv" if (m.group(1) == "1" or m.group(2) == "true") else "proj"
     for key, name in (("mlp_kernel", "mlp"), ("attention_kernel", "attention"), ("pack_kernel", "ln_prep"), ("row_stats_kernel", "ln_prep"), ("fold_kernel", "ln_prep"),
                       ("topk_kernel", "topk"), ("score_kernel", "score"),
                       ("cls_rows_kernel", "patch_embed"), ("pool_partial_kernel", "head"),
@@ -211,7 +211,11 @@ def trace_class(mangled: str):
     if "gemm_kernel" in mangled and "ELb1EE" in mangled:
         return kc + " (split-K partial)"
     if kc == "ln_prep":
-        return "ln_prep (fold)" if "fold_kernel" in mangled else "ln_prep (row stats)"
+        if "fold_kernel" in mangled:
+            return "ln_prep (fold)"
+        if "pack_kernel" in mangled:
+            return "ln_prep (weight packing)"
+        return "ln_prep (row stats)"
     return kc
 
 

@@ -358,42 +358,25 @@ rs_status run_fold(const rs_model_desc& d, const rs_block_weights* blocks, const
     for (int i = b; i < b0 + n && i < b + rs::kMaxFoldJobs / 2; ++i) {
       const rs_block_weights& w = blocks[i];
       const FoldWs fw = fold_of(d, ws, i);
-      // QKV against LayerNorm 1 (the weight-streaming kernel takes W_qkv diag(gamma1)
-      // packed in its own layout, below, and only the folded bias d from here)
-      const bool qkv_fold = !lin_qkv(d);
-      jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, qkv_fold ? fw.wq : nullptr, fw.cq, fw.dq, 3 * d.C};
+      // QKV against LayerNorm 1: W_qkv diag(gamma1) row-major with c, d for the GEMM, or
+      // packed for the weight-streaming kernel (which takes d as its bias)
+      const bool pq = lin_qkv(d);
+      jobs[nj++] = {w.w_qkv, w.ln1_g, w.ln1_b, w.b_qkv, fw.wq, fw.cq, fw.dq, 3 * d.C, pq ? 1 : 0};
+      bytes += 2.0 * 3.0 * d.C * d.C * esize(d.dtype);
       // fc1 against LayerNorm 2 (c, d vectors), unless the fused MLP kernel normalises x'
-      // itself
-      const bool fc1_fold = !rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden);
-      if (fc1_fold) jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
-      bytes += ((qkv_fold ? 2.0 : 1.0) * 3.0 * d.C + (fc1_fold ? d.hidden : 0)) * d.C * esize(d.dtype);
+      // itself; then W_proj packed for the weight-streaming kernel (a copy job: no gamma).
+      // At most two jobs per block: the packed projection comes only with the fused MLP.
+      if (!rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden)) {
+        jobs[nj++] = {w.w_fc1, w.ln2_g, w.ln2_b, w.b_fc1, nullptr, fw.c1, fw.d1, d.hidden};
+        bytes += (double)d.hidden * d.C * esize(d.dtype);
+      } else if (lin_proj_packed(d)) {
+        jobs[nj++] = {w.w_proj, nullptr, nullptr, nullptr, fw.ppack, nullptr, nullptr, d.C, 1};
+        bytes += 2.0 * d.C * d.C * esize(d.dtype);
+      }
     }
     RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
       return rs::launch_fold(dtype_of(d), jobs, nj, d.C, st);
     }));
-  }
-  // the weight-streaming kernel's packed W_qkv and W_proj
-  if (lin_qkv(d) || lin_proj_packed(d)) {
-    const bool pq = lin_qkv(d), pp = lin_proj_packed(d);
-    for (int b = b0; b < b0 + n; b += rs::kMaxLinPackJobs / 2) {
-      rs::LinPackJob jobs[rs::kMaxLinPackJobs];
-      int nj = 0;
-      double bytes = 0.0;
-      for (int i = b; i < b0 + n && i < b + rs::kMaxLinPackJobs / 2; ++i) {
-        const FoldWs fw = fold_of(d, ws, i);
-        if (pq) {
-          jobs[nj++] = {blocks[i].w_qkv, blocks[i].ln1_g, fw.wq, 3 * d.C};
-          bytes += 2.0 * rs::lin_pack_bytes(d.C, 3 * d.C);
-        }
-        if (pp) {
-          jobs[nj++] = {blocks[i].w_proj, nullptr, fw.ppack, d.C};
-          bytes += 2.0 * rs::lin_pack_bytes(d.C, d.C);
-        }
-      }
-      RS_HIP(timed(RS_KERNEL_LN_PREP, bytes, st, [&] {
-        return rs::launch_lin_pack(jobs, nj, d.C, st);
-      }));
-    }
   }
   // the fused MLP kernel's packed weights (same blocks, up to kMaxPackJobs per launch)
   if (rs::mlp_fused_supported(dtype_of(d), d.C, d.hidden)) {

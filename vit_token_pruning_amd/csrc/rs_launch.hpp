@@ -153,7 +153,7 @@ constexpr int kLinMaxN = 1536;
 struct LinArgs {
   const void* a = nullptr;      // [M][K]
   const float* stats = nullptr; // [M][stat_stride(K)] float2, or null (no LayerNorm)
-  const void* wpack = nullptr;  // W packed by launch_lin_pack (lin_pack_bytes)
+  const void* wpack = nullptr;  // W' packed by a packed fold job (lin_pack_bytes)
   const void* bias = nullptr;   // [N] bf16 (no LayerNorm)
   const float* bias_f = nullptr;// [N] fp32 (LayerNorm)
   void* out = nullptr;          // [M][ldo]
@@ -162,18 +162,11 @@ struct LinArgs {
 };
 bool lin_supported(Dtype dt, int K, int N);
 hipError_t launch_lin(Dtype dt, const LinArgs& a, int M, int K, int N, hipStream_t stream);
-// W [N][K] (times diag(gamma) when given, rounded to bf16) in the kernel's layout: per
-// 32-row slice of W, its 1 KiB MFMA register fragments in lane order (rows permuted within
-// the slice so that each lane's eight results are eight consecutive output columns).
+// W [N][K] (times diag(gamma) when given, rounded to bf16) in the kernel's layout, written
+// by launch_fold's packed jobs: per 32-row slice of W, its 1 KiB MFMA register fragments in
+// lane order (rows permuted within the slice so that each lane's eight results are eight
+// consecutive output columns).
 inline size_t lin_pack_bytes(int K, int N) { return (size_t)K * N * 2; }
-struct LinPackJob {
-  const void* w;      // [N][K]
-  const void* gamma;  // [K] or null
-  void* out;          // lin_pack_bytes(K, N)
-  int N;
-};
-constexpr int kMaxLinPackJobs = 16;
-hipError_t launch_lin_pack(const LinPackJob* jobs, int njobs, int K, hipStream_t stream);
 
 // Class-token rows of the patch embedding: out[b][0] = cls + pos[0] for b < B (rows of
 // L tokens) and their slice partials stats[b * L].
@@ -196,13 +189,14 @@ hipError_t launch_row_stats(Dtype dt, const void* x, float* stats, int M, int C,
 // the storage type with c = W' 1 (else c = W gamma).
 struct FoldJob {
   const void* w;
-  const void* gamma;
+  const void* gamma;   // null: W copied unchanged (w_out), no c, d
   const void* beta;
   const void* bias;
-  void* w_out;
+  void* w_out;         // nullable
   float* c;
   float* d;
   int rows;
+  int packed = 0;      // bf16: w_out in the weight-streaming kernel's layout (lin_pack_bytes)
 };
 constexpr int kMaxFoldJobs = 32;   // 16 blocks per launch; the arguments stay under 4 KiB
 hipError_t launch_fold(Dtype dt, const FoldJob* jobs, int njobs, int C, hipStream_t stream);

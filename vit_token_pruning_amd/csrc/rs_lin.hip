@@ -226,44 +226,6 @@ void lin_kernel(LinArgs a, int M, int N, int NSW) {
   wait_vmem<0>();   // the clamped units' direct-to-LDS loads have landed before the LDS is freed
 }
 
-// W [N][K] -> the kernel's layout: 16-byte chunk i is lane (i % 64) of fragment block
-// u = (i / 64) % (2 NKS) (k step u / 2, tile u % 2) of slice i / (128 NKS); lane (l16, g)
-// of tile t holds W row 32 slice + 8 (l16 / 4) + 4 t + l16 % 4, columns 32 (u / 2) + 8 g
-// onwards.
-struct LinPackArgs {
-  LinPackJob job[kMaxLinPackJobs];
-  int njobs, K;
-};
-__global__ __launch_bounds__(256) void lin_pack_kernel(LinPackArgs pa) {
-  const int K = pa.K, nks = K / 32;
-  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
-  size_t base = 0;
-  int j = 0;
-  for (; j < pa.njobs; ++j) {
-    const size_t n = (size_t)pa.job[j].N * K / 8;
-    if (id < base + n) break;
-    base += n;
-  }
-  if (j == pa.njobs) return;
-  const LinPackJob& jb = pa.job[j];
-  const size_t i = id - base;
-  const int per_slice = 128 * nks;
-  const int sc = (int)(i / per_slice), rem = (int)(i % per_slice);
-  const int u = rem >> 6, lane = rem & 63, l16 = lane & 15, g = lane >> 4;
-  const int s = u >> 1, t = u & 1;
-  const int row = sc * kLinSlice + 8 * (l16 >> 2) + 4 * t + (l16 & 3), col = 32 * s + 8 * g;
-  Frag8<bf16> f;
-  load_frag(f, static_cast<const bf16*>(jb.w) + (size_t)row * K + col);
-  if (jb.gamma) {
-    float w[8], gm[8];
-    frag_to_f32(f, w);
-    load8f(static_cast<const bf16*>(jb.gamma) + col, gm);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[e] = pack_bf16x2(w[2 * e] * gm[2 * e], w[2 * e + 1] * gm[2 * e + 1]);
-  }
-  store_frag(static_cast<char*>(jb.out) + i * 16, f);
-}
-
 template <int NKS>
 hipError_t launch_lin_nks(const LinArgs& a, int M, int N, hipStream_t st) {
   // Rows alone give M / 128 workgroups, too few to fill the chip at most token counts;
@@ -308,22 +270,6 @@ hipError_t launch_lin(Dtype dt, const LinArgs& a, int M, int K, int N, hipStream
     case 6: return launch_lin_nks<12>(a, M, N, st);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_lin_pack(const LinPackJob* jobs, int njobs, int K, hipStream_t st) {
-  if (njobs < 1 || njobs > kMaxLinPackJobs || K % 64 != 0 || K < 64 || K > kMlpMaxWidth)
-    return hipErrorInvalidValue;
-  LinPackArgs pa;
-  size_t total = 0;
-  for (int j = 0; j < njobs; ++j) {
-    if (jobs[j].N % kLinSlice != 0 || jobs[j].N <= 0) return hipErrorInvalidValue;
-    pa.job[j] = jobs[j];
-    total += (size_t)jobs[j].N * K / 8;
-  }
-  pa.njobs = njobs;
-  pa.K = K;
-  lin_pack_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(pa);
-  return hipGetLastError();
 }
 
 }  // namespace rs

@@ -67,9 +67,13 @@ static_assert(sizeof(FoldArgs) <= 4096, "kernel arguments are limited to 4 KiB")
 
 // 16 lanes per output row n of one job (four rows per wave): W'[n][k] = W[n][k] * gamma[k]
 // (rounded to the storage type; only if the job has an output), c[n] = sum_k W'[n][k] (or
-// the unrounded sum_k W[n][k] gamma[k]), d[n] = sum_k W[n][k] beta[k] + b[n].  Lane s of
-// a row takes 8-element chunks s, s + 16, ... (at most 8 for C <= 1024) and requests all
-// of them before using any, so a wave keeps up to 32 row chunks in flight.
+// the unrounded sum_k W[n][k] gamma[k]), d[n] = sum_k W[n][k] beta[k] + b[n].  A job
+// without gamma copies W unchanged (no c, d).  A packed job (bf16) writes W' in the
+// weight-streaming linear kernel's layout instead of row-major: 8-element chunk ch of row n
+// goes to slice n / 32, fragment block 2 (ch / 4) + t, lane 16 (ch % 4) + l16, where row
+// n % 32 = 8 (l16 / 4) + 4 t + l16 % 4.  Lane s of a row takes 8-element chunks s, s + 16,
+// ... (at most 8 for C <= 1024) and requests all of them before using any, so a wave keeps
+// up to 32 row chunks in flight.
 constexpr int kFoldLanes = 16, kFoldRowsPerBlock = 256 / kFoldLanes;
 template <typename T>
 __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
@@ -85,8 +89,12 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
   while (j + 1 < fa.njobs && rr >= fa.rows_before[j + 1]) ++j;
   const FoldJob& jb = fa.job[j];
   const int n = rr - fa.rows_before[j], C = fa.C, nch = C >> 3;
+  const bool fold = jb.gamma != nullptr;
   const T* w = static_cast<const T*>(jb.w) + (size_t)n * C;
-  T* wo = jb.w_out && live ? static_cast<T*>(jb.w_out) + (size_t)n * C : nullptr;
+  char* wo = jb.w_out && live ? static_cast<char*>(jb.w_out) : nullptr;
+  // packed layout: this row's place within its slice
+  const int n32 = n & 31, pt = (n32 >> 2) & 1, pl16 = 4 * (n32 >> 3) + (n32 & 3);
+  const size_t pslice = (size_t)(n >> 5) * (C >> 5) * 2 * 1024;
   Frag8<T> raw[kMaxCh];
 #pragma unroll
   for (int i = 0; i < kMaxCh; ++i) {
@@ -100,19 +108,33 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs fa) {
     if (ch >= nch) break;
     float wv[8], g[8], b[8], o[8];
     frag_to_f32(raw[i], wv);
-    load8f(static_cast<const T*>(jb.gamma) + ch * 8, g);
-    load8f(static_cast<const T*>(jb.beta) + ch * 8, b);
+    if (fold) {
+      load8f(static_cast<const T*>(jb.gamma) + ch * 8, g);
+      load8f(static_cast<const T*>(jb.beta) + ch * 8, b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] = jb.w_out ? round_t<T>(wv[e] * g[e]) : wv[e] * g[e];
-      c += o[e];
-      d = fmaf(wv[e], b[e], d);
+      for (int e = 0; e < 8; ++e) {
+        o[e] = jb.w_out ? round_t<T>(wv[e] * g[e]) : wv[e] * g[e];
+        c += o[e];
+        d = fmaf(wv[e], b[e], d);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = wv[e];
     }
-    if (wo) store8f(wo + ch * 8, o);
+    if (wo) {
+      if constexpr (sizeof(T) == 2) {
+        if (jb.packed) {
+          const size_t off = pslice + (size_t)(2 * (ch >> 2) + pt) * 1024 + ((ch & 3) * 16 + pl16) * 16;
+          store8f(reinterpret_cast<T*>(wo + off), o);
+          continue;
+        }
+      }
+      store8f(reinterpret_cast<T*>(wo) + (size_t)n * C + ch * 8, o);
+    }
   }
-  c = sum16(c);
+  c = sum16(c);   // (every row's 16 lanes take part; a copy job's sums are unused)
   d = sum16(d);
-  if (sub == 0 && live) {
+  if (fold && sub == 0 && live) {
     jb.c[n] = c;
     jb.d[n] = d + to_f32(static_cast<const T*>(jb.bias)[n]);
   }
