@@ -107,9 +107,9 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
   // W1 rows (k step u / 2, row tile u % 2), blocks 2 NKS + j slice c's W2 columns for
   // output tile j.  Block u of a slice is 1 KiB of the packed weights (lane l's MFMA
   // operand at 16 l), so each direct load copies 1 KiB of consecutive bytes.  Waves 0-3
-  // load the W1 blocks, waves 4-7 the W2 blocks.  Slices past the end are clamped to the
-  // last one: their blocks are loaded (so every unit is the same NLOAD loads per wave and
-  // the waits below count correctly) but never read.
+  // load the W1 blocks, waves 4-7 the W2 blocks.  The W1 blocks of the last two units name
+  // slices past the end; they are clamped to the last slice (loaded, so every unit is the
+  // same NLOAD loads per wave, and read by fc1 work whose results are not used).
   const bool w1side = wave < kMlpWaves / 2;
   const char* gbase = static_cast<const char*>(a.wpack) + (size_t)wave * NLOAD * 1024 + lane * 16;
   auto stage = [&](int sc, char* lds_base) {
@@ -246,7 +246,8 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
   // product).
   constexpr int NQ = 4 * NKS, kDepth = 6;
   for (int c = 0; c < NC; ++c) {
-    wait_vmem<NLOAD>();  // this wave's blocks of unit c have landed (unit c + 1 may not)
+    // this wave's blocks of unit c have landed (unit c + 1, if there is one, may not)
+    if (c + 1 < NC) wait_vmem<NLOAD>(); else wait_vmem<0>();
     barrier_nofence();   // ... and every wave's; unit c - 1's buffer is no longer read
     const char* us = lb + bufp(c);
     auto faddr = [&](int q) { return us + ((q & 1) ? W1B + (q >> 1) * 1024 : (q >> 1) * 1024); };
@@ -286,17 +287,19 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
     for (int e = 0; e < 4; ++e) hbuf.v[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
     hp0 = h0;
     hp1 = h1;
-    stage_unit(c + 2);   // into the buffer unit c - 1 used
+    // into the buffer unit c - 1 used; units past the last are not loaded (the epilogue's
+    // row loads would otherwise wait for them: loads complete in issue order)
+    if (c + 2 < NC) stage_unit(c + 2);
   }
 
   // ---- epilogue: acc[2 J + t][r] = y - b2 of row m, output column 32 J + 8 g + 4 t + r.
   // y = MLP(LN(x')); x' = x + p re-formed in fp32; x_hat = x' + y stored; the shift
   // partials and the stored row's statistics per 64-column slice (J = 2 sl, 2 sl + 1),
-  // summed over the token's 4 lanes.  x and p of slice sl + 1 are requested before slice sl
+  // summed over the token's 4 lanes.  x and p of slice sl + 2 are requested before slice sl
   // is computed.
   const int nsl = C / 64, sstride = stat_stride(C);
   bf16* out = static_cast<bf16*>(a.out);
-  Frag8<bf16> ex[2][2], epp[2][2];        // [buffer][J within the slice]
+  Frag8<bf16> ex[3][2], epp[3][2];        // [buffer][J within the slice]
   auto load_slice = [&](int sl, int b) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -306,16 +309,17 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
     }
   };
   load_slice(0, 0);
+  if (1 < nsl) load_slice(1, 1);
 #pragma unroll
   for (int sl = 0; sl < nsl; ++sl) {
-    if (sl + 1 < nsl) load_slice(sl + 1, (sl + 1) & 1);
+    if (sl + 2 < nsl) load_slice(sl + 2, (sl + 2) % 3);
     float w[16], s0 = 0.f, s1 = 0.f, s2 = 0.f, cs[2] = {0.f, 0.f};
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int J = 2 * sl + h2, n = 32 * J + 8 * g;
       float xv[8], pv[8], bb[8];
-      frag_to_f32(ex[sl & 1][h2], xv);
-      frag_to_f32(epp[sl & 1][h2], pv);
+      frag_to_f32(ex[sl % 3][h2], xv);
+      frag_to_f32(epp[sl % 3][h2], pv);
       frag_to_f32(lds_frag(b2tab + n * 2), bb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -377,14 +381,14 @@ void mlp_kernel(MlpArgs a, int M, int Hd) {
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);   // one slice's loads ahead, not all of them
+    __builtin_amdgcn_sched_barrier(0);   // two slices' loads ahead, not all of them
   }
   // partial slots past the last 64-column slice (the score reads nparts per quantity)
   if (a.part && ok && g == 0) {
     for (int q = 0; q < (a.dist == 2 ? 3 : 1); ++q)
       for (int sl = nsl; sl < a.nparts; ++sl) a.part[mc * a.pstride + q * a.nparts + sl] = 0.f;
   }
-  wait_vmem<0>();   // the two clamped units' direct-to-LDS loads have landed before the LDS is freed
+  wait_vmem<0>();
 }
 
 // Packing of W1 / W2 into the fused kernel's fragment order: 16-byte chunk i of a block's
