@@ -309,15 +309,20 @@ const char* rs_last_error(void);
  * time (launches of the two encoder lanes may overlap, and each then includes the time
  * it shared the GPU), the number of launches and the summed algorithmic work of those launches
  * (flop for the GEMM and attention kernels, bytes for the memory-bound ones).
- * LayerNorm has no pass of its own: it is folded into the QKV and fc1 GEMMs, whose inputs'
- * row statistics come from the producing epilogue; RS_KERNEL_LN_PREP times the remaining
- * preparation (statistics of the encoder input, per-call weight folding).
+ * LayerNorm has no pass of its own: it is applied inside the kernel that consumes it (the
+ * QKV kernel and the fused MLP for bf16 widths up to 384, folded into the QKV and fc1 GEMMs
+ * otherwise), from row statistics written by the producing kernel; RS_KERNEL_LN_PREP times
+ * the remaining preparation (statistics of the encoder input, per-call weight folding and
+ * packing).
  * One timing session at a time per process. */
 typedef enum {
-  RS_KERNEL_LN_PREP = 0,      /* LayerNorm statistics and weight folding */
-  RS_KERNEL_QKV = 1,
+  RS_KERNEL_LN_PREP = 0,      /* LayerNorm statistics, weight folding and packing */
+  RS_KERNEL_QKV = 1,          /* LayerNorm 1 + QKV projection (weight-streaming kernel for
+                                 bf16, C <= 384; GEMM otherwise) */
   RS_KERNEL_ATTENTION = 2,
-  RS_KERNEL_PROJ = 3,
+  RS_KERNEL_PROJ = 3,         /* attention output projection (weight-streaming kernel when
+                                 the MLP is fused and the attention-sublayer shift is not
+                                 the score; GEMM otherwise) */
   RS_KERNEL_FC1 = 4,
   RS_KERNEL_FC2_SCORE = 5,
   RS_KERNEL_TOPK = 6,
