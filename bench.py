@@ -347,12 +347,18 @@ def summarize_standalone(dirs, workload):
 
 
 def kernel_sources_sha256():
+    """Hash of the library's sources as code: comments and whitespace are dropped, so a
+    profile stays tied to the code it measured when only the prose around it changes."""
     import hashlib
+    import re
     src = os.path.join(ROOT, "vit_token_pruning_amd", "csrc")
     h = hashlib.sha256()
+    strip = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
     for f in sorted(os.listdir(src)):
         if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(src, f), "rb").read())
+            text = open(os.path.join(src, f), encoding="utf-8").read()
+            code = strip.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+            h.update(f.encode() + b"\0" + " ".join(code.split()).encode() + b"\0")
     return h.hexdigest()
 
 

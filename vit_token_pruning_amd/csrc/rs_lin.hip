@@ -1,18 +1,21 @@
 // The two linear layers of the attention sublayer for widths C <= 384 in bf16, weights
-// streamed through LDS: the QKV projection with LayerNorm 1 computed in the kernel (Eq. (5)
+// streamed through LDS: the QKV projection with LayerNorm 1 applied in the kernel (Eq. (5)
 // of "Representation Shift: Unifying Token Compression with FlashAttention", arXiv HTML,
 // Sec. 3.3, feeds LN(x) to self-attention, whose queries, keys and values are linear maps
 // of its input, Sec. 3.1 Eq. (1)), and the attention output projection (the term Eq. (5)
 // adds to x).
 //
-// out[m][n] = A'[m] . W[n] + b[n], A' the row's LayerNorm (fp32 statistics, one rounding
-// to bf16) or the row as given.  A workgroup of 4 waves owns 128 rows; each wave keeps its
-// 32 rows (two 16-row groups) as MFMA B operands in registers (C / 4 VGPRs) and walks the
-// N outputs in slices of 32, whose W rows the workgroup stages in LDS from a per-call
-// packed copy: staged row 16 t + 4 g' + r of a slice holds output 8 g' + 4 t + r, so lane
-// group g ends with outputs 8 g .. 8 g + 7 and stores them as one 16-byte piece.  Each
-// fragment read from LDS feeds the products of both row groups.  Three 24 KiB units at
-// C = 384 (slice c is read while c + 1 and c + 2 load) leave room for two workgroups per CU.
+// out[m][n] = A'[m] . W'[n] + b'[n].  QKV: A' = (x - mean) * rstd of the row, from the
+// slice partials its producer wrote, rounded once to bf16; W' = W diag(gamma1) and
+// b' = b + W beta1 (fp32) come from the LayerNorm fold pass, so LN(x) W^T + b is computed.
+// Projection: A' = the row, W' = W, b' = b.  A workgroup of 4 waves owns 128 rows; each
+// wave keeps its 32 rows (two 16-row groups) as MFMA B operands in registers (C / 4 VGPRs)
+// and walks its range of the N outputs in slices of 32, whose W' rows the workgroup stages
+// in LDS from the packed copy: staged row 16 t + 4 g' + r of a slice holds output
+// 8 g' + 4 t + r, so lane group g ends with outputs 8 g .. 8 g + 7 and stores them as one
+// 16-byte piece.  Each fragment read from LDS feeds the products of both row groups.
+// Three 24 KiB units at C = 384 (slice c is read while c + 1 and c + 2 load) and a 6 KiB
+// bias table leave room for two workgroups per CU.
 #include "rs_device.hpp"
 #include "rs_launch.hpp"
 
