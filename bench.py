@@ -725,7 +725,7 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the single-lane per-kernel breakdown and every context pass, so "
                          "every launch in the process is a timed-mode launch (for profiler runs)")
-    ap.add_argument("--kernel", default="mlp", choices=[k for k in ("ln_prep", "qkv", "attention",
+    ap.add_argument("--kernel", default=None, choices=[k for k in ("ln_prep", "qkv", "attention",
                     "proj", "fc1", "fc2_score", "mlp", "topk")],
                     help="roofline kernel when --no-breakdown is given")
     ap.add_argument("--no-compare", action="store_true",
@@ -810,7 +810,11 @@ def main():
     # BREAKDOWN_STEPS steps per class; fc1 and fc2 are close at DeiT-S)
     per, kt1 = {}, None
     if args.no_breakdown:
-        dominant = args.kernel
+        # the kernel named, else the MLP sublayer's: the fused kernel where it runs (bf16,
+        # C <= 384), the fc2 GEMM otherwise
+        fused = wl.dtype == "bf16" and 64 <= wl.C <= 384 and wl.C % 64 == 0 and \
+            wl.hidden % 32 == 0 and 64 <= wl.hidden <= 4096
+        dominant = args.kernel or ("mlp" if fused else "fc2_score")
     else:
         per = breakdown(enc, x, rs, BREAKDOWN_STEPS)
         dominant = max(per, key=lambda k: per[k]["ms"])
@@ -826,7 +830,7 @@ def main():
     # instrumentation costs
     with rs.KernelTimer(dominant) as kt:
         ms_instr = time_steps(lambda: enc.forward(x), args.steps, torch)
-    achieved = rate(kt.work, kt.total_ms)
+    achieved = rate(kt.work, kt.total_ms) if kt.total_ms > 0 else 0.0
     roof = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK[bound],
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(achieved / PEAK[bound], 4),
             "traffic": stored_traffic(wl.name, dominant),
