@@ -102,6 +102,15 @@ def test_encoder_full_size(name):
     check_encoder(synth.WORKLOADS[name], SAMPLED[name])
 
 
+def test_encoder_full_size_ragged_rows():
+    """DeiT-S at its full length and depth with 250 samples: lanes of 125 samples, so every
+    stage's rows (125 x 197, x 138, x 97, x 68) end in a partial 128-row block of the
+    weight-streaming QKV / projection kernel and the fused MLP."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["deit_s"], B=250)
+    check_encoder(wl, [0, 249])
+
+
 @pytest.mark.parametrize("B", [1, 3, 45])
 def test_encoder_one_lane_and_uneven_lanes(B):
     """B = 1 and 3 run on the caller's stream alone (too few rows for two lanes); B = 45
